@@ -1,0 +1,182 @@
+"""Benchmark: MoE layer tokens/s at 16K-token prefill on one MI355X, plus the
+grouped-GEMM MXFP8 MFMA fraction of peak.
+
+Workload: T=16384 tokens, K=2048, I=768, E=128, top-8 near-uniform routing,
+offline pre-quantised e4m3 expert weights with e8m0 pair-split scales
+(synthetic, seeded; see workloads/).  Inputs and weights are resident in HBM
+before timing starts.  One step = one moe_mxfp8_forward call over the whole
+batch: routing + fused MX activation quant, GEMM1 + SwiGLU + requant, GEMM2,
+finalize.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+
+Prints one JSON line.  After the headline loop a second loop runs the same
+four kernels through their own entry points with HIP events between them (on
+the stream they run on) to get each kernel's average duration; the roofline
+object is computed from those.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mxfp8_block_scaled_topk_amd as mx  # noqa: E402
+from workloads import CONFIGS, make_inputs  # noqa: E402
+
+MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8/MXFP8 MFMA
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
+CFG = CONFIGS["prefill"]
+
+# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of the GEMM1 kernel, per launch,
+# scaled by the copy-kernel calibration (see profiles/); None until measured
+# for the current kernel.
+GEMM1_TRAFFIC_BYTES = None
+
+
+def algorithmic(cfg, counts):
+    """Per-launch algorithmic FLOPs and bytes of each kernel."""
+    T, K, I, E, k = cfg.T, cfg.K, cfg.I, cfg.E, cfg.k
+    M = T * k
+    e_act = int((counts > 0).sum())
+    w13 = E * 2 * I * K * (1 + 1 / 32)
+    w2 = E * K * I * (1 + 1 / 32)
+    return {
+        "route_quant": {"bytes": 2 * T * K + 4 * T * k + M * K * (1 + 1 / 32) + 8 * M + 8 * E},
+        "gemm1_swiglu_requant": {"flops": 2 * M * 2 * I * K,
+                                 "bytes": M * K * (1 + 1 / 32) + e_act / E * w13 + M * I * (1 + 1 / 32)},
+        "gemm2": {"flops": 2 * M * K * I, "bytes": M * I * (1 + 1 / 32) + e_act / E * w2 + 2 * M * K},
+        "finalize": {"bytes": 2 * M * K + 8 * T * k + 2 * T * K},
+    }
+
+
+def cpu_baseline(d, tokens=2048):
+    """The oracle, as it stands, on the first `tokens` tokens of the workload."""
+    from oracle import moe_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    t0 = time.perf_counter()
+    moe_ref.moe_forward_ref(d["x"][:tokens], d["topk_ids"][:tokens], d["topk_w"][:tokens], d["w13q"], d["w13s"],
+                            d["w2q"], d["w2s"])
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {tokens} of {CFG.T} tokens of the same workload (all {CFG.E} experts), "
+                      f"full oracle layer, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (one GPU holds all experts); "
+              "--gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    cfg = CFG
+    T, K, I, E, k = cfg.T, cfg.K, cfg.I, cfg.E, cfg.k
+    d = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    ids = torch.from_numpy(d["topk_ids"]).to(dev)
+    w = torch.from_numpy(d["topk_w"]).to(dev)
+    w13, w13s, w2, w2s = (torch.from_numpy(d[n]).to(dev) for n in ("w13q", "w13s", "w2q", "w2s"))
+    out = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+    ws = mx.forward_workspace(T, K, I, E, k, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mx.moe_mxfp8_forward(x, ids, w, w13, w13s, w2, w2s, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+
+    # ---- per-kernel durations: the same four kernels, events between them ----
+    inter = mx.forward_intermediates(ws, T, K, I, E, k)
+    counts = inter["group_list"].cpu().numpy()
+    rws = torch.empty(mx.route_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
+    route_out = (inter["xq"], inter["xs"], inter["sorted_row"], inter["expanded_row_idx"], inter["group_list"])
+    names = ["route_quant", "gemm1_swiglu_requant", "gemm2", "finalize"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record(stream)
+        mx.moe_route_quant(x, ids, E, out=route_out, workspace=rws)
+        e[1].record(stream)
+        mx.gmm_swiglu_mxquant(inter["xq"], inter["xs"], w13, w13s, inter["group_list"], 1,
+                              out=(inter["hq"], inter["hs"]))
+        e[2].record(stream)
+        mx.gmm_mx(inter["hq"], inter["hs"], w2, w2s, inter["group_list"], 1, out=inter["y"])
+        e[3].record(stream)
+        mx.moe_finalize(inter["y"], w, inter["expanded_row_idx"], out=out)
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    dur = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)])) * 1e-3
+           for i, n in enumerate(names)}
+    alg = algorithmic(cfg, counts)
+    kernels = {}
+    for n in names:
+        a = alg[n]
+        kd = {"avg_us": round(dur[n] * 1e6, 2), "hbm_GBs": round(a["bytes"] / dur[n] / 1e9, 1),
+              "hbm_frac": round(a["bytes"] / dur[n] / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": int(a["bytes"])}
+        if "flops" in a:
+            tf = a["flops"] / dur[n] / 1e12
+            kd.update({"TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_FP8_PEAK_TFLOPS, 4),
+                       "alg_flops": int(a["flops"])})
+        kernels[n] = kd
+    g1, g2 = alg["gemm1_swiglu_requant"], alg["gemm2"]
+    gemm_tflops = (g1["flops"] + g2["flops"]) / (dur["gemm1_swiglu_requant"] + dur["gemm2"]) / 1e12
+    dom = "gemm1_swiglu_requant"
+    achieved = g1["flops"] / dur[dom] / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
+                "traffic": GEMM1_TRAFFIC_BYTES}
+
+    rec = {
+        "metric": "MoE layer tokens/s @16K prefill; grouped-GEMM MXFP8 MFMA % of peak",
+        "value": round(T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": "16K-token prefill MoE layer, offline pre-quantised MXFP8 experts",
+                   "T": T, "K": K, "I": I, "E": E, "top_k": k, "global_batch": T, "parallelism": "none"},
+        "grouped_gemm_mfma_frac": round(gemm_tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+        "grouped_gemm_TFLOPs": round(gemm_tflops, 1),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(d)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+/*
+ * mxmoe.h -- C ABI of the MXFP8 block-scaled top-k MoE expert layer for
+ * AMD MI355X (gfx950).
+ *
+ * The layer (sources: "Quantization on Ascend", sglang docs, section on MXFP8
+ * for LLM MoE models; "[WIP] Fix offline W8A8 MXFP8 quantization for Qwen3.5
+ * on Ascend NPU", sglang PR 32266, commit adding the fused-experts chain):
+ *
+ *   moe_route_quant     top-k routing with the MX activation quant fused in
+ *   gmm_swiglu_mxquant  grouped GEMM1 (gate + up) + SwiGLU + MX requant
+ *   gmm_mx              grouped GEMM2 (down), bf16 output
+ *   moe_finalize        weighted un-permute and sum of the top-k outputs
+ *   moe_mxfp8_forward   the four steps above on one stream
+ *   mx_quantize         stand-alone MX quantiser (weights at load time)
+ *
+ * Formats.  MXFP8 = e4m3 payload bytes plus one e8m0 scale byte (exponent +
+ * 127, value 2^(byte-127)) per 32 consecutive elements along the reduction
+ * dimension.  A row of Kd elements has ceil(Kd/32) scales, padded with one
+ * zero byte when that count is odd, stored as [ceil(Kd/64), 2] pairs: the
+ * pair-split layout ("Quantization on Ascend", offline MoE path: [E,N,K/32]
+ * scales viewed as [E,N,K/64,2]; PR 32266 Summary, offline partial block-scale
+ * layout, worked example K = 4304 -> 135 -> 136 -> 68 pairs).  There is no zero
+ * point.  Quantisation: s = floor(log2(amax)) - 8 clamped to [-127, 127]
+ * (scale byte s + 127; an all-zero block gets byte 0), payload = e4m3 of
+ * x * 2^-s rounded to nearest, ties to even, saturating at +-448, sign kept
+ * (so -0 and negative values that round to zero give 0x80).
+ *
+ * Tensors.  Every pointer is a DEVICE pointer unless stated; all tensors are
+ * dense row-major.  bf16 is passed as its 16-bit pattern.  Sizes are int64_t.
+ *   x            bf16   [T, K]
+ *   topk_ids     int32  [T, k]   expert ids in [0, E)
+ *   topk_w       fp32   [T, k]   routing weights
+ *   w13          uint8  [E, 2I, K]   e4m3; rows [0, I) gate, rows [I, 2I) up
+ *   w13_s        uint8  [E, 2I, K/64, 2]
+ *   w2           uint8  [E, K, I]    e4m3
+ *   w2_s         uint8  [E, K, I/64, 2]
+ *   group_list   int64  [E]  type 1: rows per expert (counts);
+ *                            type 0: inclusive cumulative counts
+ *   M = T*k expanded rows; expert e owns a contiguous run of rows in expert
+ *   order, and inside one expert rows keep the order of the flat assignment
+ *   index t*k + j (a stable sort).
+ *
+ * Ownership and execution.  The caller allocates every buffer, including
+ * the workspaces (sized by the *_workspace_size queries).  The library never
+ * allocates, frees or retains pointers and never synchronises the host.
+ * Every call enqueues work on `stream` (a hipStream_t passed as void*; NULL =
+ * the null stream) and returns at once; results are ready when the stream
+ * reaches them.  Calls on different streams must not share output or
+ * workspace buffers.
+ *
+ * Errors.  Every entry point returns MX_OK (0) or a negative mx_status.
+ * Argument checks happen on the host before anything is enqueued; on error
+ * nothing is enqueued and mx_last_error() (thread-local) describes why.
+ * Data-dependent conditions are handled on the device without faulting:
+ * an expert id outside [0, E) is dropped (its expanded_row_idx entry is -1,
+ * it counts toward no expert, so sum(group_list) < T*k tells the caller), and
+ * group lists are clamped to [0, M] rows.
+ *
+ * GPU shape limits (MX_ERR_UNSUPPORTED otherwise): GEMM reduction and output
+ * dims (K, I, N, Kd of the GEMMs) multiples of 128; routing needs K % 32 == 0
+ * and 1 <= k <= 256, E <= 1024; mx_quantize takes any Kd >= 1.
+ */
+#ifndef MXMOE_H
+#define MXMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mx_status {
+  MX_OK = 0,
+  MX_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, k > E, bad group_list_type */
+  MX_ERR_UNSUPPORTED = -2, /* a shape the GPU kernels do not handle (see above) */
+  MX_ERR_WORKSPACE = -3,   /* workspace smaller than the size query returned */
+  MX_ERR_HIP = -4          /* a HIP runtime error at launch */
+} mx_status;
+
+/*
+ * MX-quantise `rows` rows of `kd` bf16 elements (row stride `ld` elements,
+ * ld >= kd) into e4m3 payload q [rows, kd] (row stride kd bytes) and scales
+ * s [rows, ceil(kd/64), 2] (odd scale counts padded with a zero byte).
+ * Used on expert weights at load time ("Quantization on Ascend", MoE online
+ * path: bf16 [E, N, K] expert weights quantised once, 3-D input taken as
+ * E*N rows) and for activations that bypass routing.
+ */
+int mx_quantize(const void* x_bf16, int64_t rows, int64_t kd, int64_t ld,
+                void* q_u8, void* s_u8, void* stream);
+
+/* Workspace bytes moe_route_quant needs for T tokens, top-k, E experts. */
+size_t moe_route_quant_workspace_size(int64_t T, int64_t k, int64_t E);
+
+/*
+ * Top-k routing with fused MX activation quant ("Quantization on Ascend",
+ * MoE forward: routing quantises the activations in the same op; PR 32266,
+ * commit on the fused routing quant: byte-identical to routing then
+ * quantising).  Outputs, for M = T*k:
+ *   xq                uint8 [M, K]        row p = MX payload of token sorted_row[p] / k
+ *   xs                uint8 [M, K/64, 2]  its scales (pair-split)
+ *   sorted_row        int32 [M]           flat assignment index t*k+j of row p
+ *   expanded_row_idx  int32 [M]           row p of flat assignment i (-1 if its id was invalid)
+ *   group_list        int64 [E]           rows per expert (count form, type 1)
+ * Rows past sum(group_list) (only when ids were invalid) are left unwritten.
+ */
+int moe_route_quant(const void* x_bf16, const int32_t* topk_ids,
+                    int64_t T, int64_t K, int64_t k, int64_t E,
+                    void* xq_u8, void* xs_u8, int32_t* sorted_row,
+                    int32_t* expanded_row_idx, int64_t* group_list,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped GEMM1 with SwiGLU and MX requant fused ("Quantization on Ascend",
+ * MoE forward: GEMM1 fuses gate/up, SwiGLU and requant and hands back
+ * quantised activations plus block scales; "PR #30768 report", key source
+ * excerpt: it takes a cumulative group list, the dispatcher produces counts).
+ * For expert e and its rows m:
+ *   acc = A[m] . W13_e^T (fp32 accumulation), g = acc[:, :I], u = acc[:, I:],
+ *   h = silu(g) * u (fp32), (hq, hs) = MX quantisation of h along I.
+ *   a      uint8 [M, K], a_s [M, K/64, 2]
+ *   hq     uint8 [M, I], hs  [M, I/64, 2]
+ *   h_f32_debug  fp32 [M, I] or NULL: when given, also receives h.
+ * group_list_type: 0 = cumulative, 1 = count.  Rows not owned by any expert
+ * are not written.
+ */
+int gmm_swiglu_mxquant(const void* a_u8, const void* a_s,
+                       const void* w13_u8, const void* w13_s,
+                       const int64_t* group_list, int group_list_type,
+                       int64_t M, int64_t K, int64_t I, int64_t E,
+                       void* hq_u8, void* hs_u8, float* h_f32_debug,
+                       void* stream);
+
+/*
+ * Grouped MX GEMM with bf16 output (GEMM2, down projection; "Quantization on
+ * Ascend", MoE forward: the second grouped GEMM takes the count group list).
+ *   y[m, :] = bf16_rne( A[m] . W_e^T )  for the expert e owning row m
+ *   a  uint8 [M, Kd], a_s [M, Kd/64, 2];  w uint8 [E, N, Kd], w_s [E, N, Kd/64, 2]
+ *   y  bf16 [M, N]
+ */
+int gmm_mx(const void* a_u8, const void* a_s, const void* w_u8, const void* w_s,
+           const int64_t* group_list, int group_list_type,
+           int64_t M, int64_t N, int64_t Kd, int64_t E,
+           void* y_bf16, void* stream);
+
+/*
+ * Finalize: weighted un-permute and sum (PR 32266, fused-experts commit:
+ * the chain ends with finalize routing).
+ *   out[t, :] = bf16_rne( sum_{j=0}^{k-1} w[t, j] * y[expanded_row_idx[t*k+j], :] )
+ * accumulated in fp32 in ascending j, each product and sum rounded to fp32.
+ * Entries whose index is outside [0, M) are skipped.
+ *   y bf16 [M, K], topk_w fp32 [T, k], expanded_row_idx int32 [T*k], out bf16 [T, K]
+ */
+int moe_finalize(const void* y_bf16, const float* topk_w,
+                 const int32_t* expanded_row_idx, int64_t T, int64_t K,
+                 int64_t k, int64_t M, void* out_bf16, void* stream);
+
+/* Workspace bytes moe_mxfp8_forward needs (holds every intermediate). */
+size_t moe_mxfp8_forward_workspace_size(int64_t T, int64_t K, int64_t I,
+                                        int64_t E, int64_t k);
+
+/*
+ * The whole layer on one stream: moe_route_quant -> gmm_swiglu_mxquant ->
+ * gmm_mx -> moe_finalize (PR 32266, fused-experts commit; "Quantization on
+ * Ascend", MoE forward).  Weights are pre-quantised (see mx_quantize).
+ * out bf16 [T, K].  Intermediates live in the workspace.
+ */
+int moe_mxfp8_forward(const void* x_bf16, const int32_t* topk_ids,
+                      const float* topk_w, const void* w13_u8,
+                      const void* w13_s, const void* w2_u8, const void* w2_s,
+                      int64_t T, int64_t K, int64_t I, int64_t E, int64_t k,
+                      void* out_bf16, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/* Byte offsets of the intermediates inside the forward workspace, so a caller
+ * can inspect them after the stream has run.  Fills the 8 offsets in order:
+ * xq, xs, sorted_row, expanded_row_idx, group_list, hq, hs, y. */
+int moe_mxfp8_forward_workspace_layout(int64_t T, int64_t K, int64_t I,
+                                       int64_t E, int64_t k,
+                                       size_t* offsets_host);
+
+/* Description of the last non-OK status returned on this thread. */
+const char* mx_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXMOE_H */

@@ -1,0 +1,270 @@
+"""Python binding of libmxmoe.so, the MXFP8 block-scaled top-k MoE expert
+layer for AMD MI355X (gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+Tensors are torch tensors on the GPU (torch supplies device memory and the
+current stream); outputs are allocated here when not passed in.  Any non-OK
+status from the library raises ``MxError`` with the library's message.
+
+Formats (see include/mxmoe.h): e4m3 payloads and e8m0 scales are uint8
+tensors; scales use the pair-split layout [rows, ceil(cols/64), 2]; bf16
+tensors are torch.bfloat16; group lists are int64 (type 1 = counts,
+type 0 = inclusive cumulative counts).
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MxError", "lib_path", "load", "mx_quantize", "moe_route_quant", "gmm_swiglu_mxquant",
+    "gmm_mx", "moe_finalize", "moe_mxfp8_forward", "forward_workspace", "forward_intermediates",
+    "route_workspace_size", "forward_workspace_size", "last_error",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+MX_OK = 0
+GROUP_CUMULATIVE = 0
+GROUP_COUNT = 1
+
+
+class MxError(RuntimeError):
+    """A non-OK status from libmxmoe."""
+
+
+def lib_path():
+    return os.path.join(_HERE, "libmxmoe.so")
+
+
+def load():
+    """Load libmxmoe.so (built by ``python -m mxfp8_block_scaled_topk_amd.build``).
+
+    There is no fallback: a missing library is an error."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise MxError(f"{path} is missing; build it with `python -m mxfp8_block_scaled_topk_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "mx_quantize": (I32, [P, I64, I64, I64, P, P, P]),
+        "moe_route_quant_workspace_size": (SZ, [I64, I64, I64]),
+        "moe_route_quant": (I32, [P, P, I64, I64, I64, I64, P, P, P, P, P, P, SZ, P]),
+        "gmm_swiglu_mxquant": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P, P, P]),
+        "gmm_mx": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]),
+        "moe_finalize": (I32, [P, P, P, I64, I64, I64, I64, P, P]),
+        "moe_mxfp8_forward_workspace_size": (SZ, [I64, I64, I64, I64, I64]),
+        "moe_mxfp8_forward": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
+        "moe_mxfp8_forward_workspace_layout": (I32, [I64, I64, I64, I64, I64, P]),
+        "mx_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def last_error():
+    return load().mx_last_error().decode()
+
+
+def _check(rc, what):
+    if rc != MX_OK:
+        raise MxError(f"{what}: status {rc}: {last_error()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _need_contig(t, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _pairs(n):
+    return -(-n // 64)
+
+
+def mx_quantize(x, q=None, s=None, stream=None):
+    """MX-quantise the last dim of a bf16 tensor [..., Kd] (rows may be strided
+    with unit inner stride).  Returns (q uint8 [..., Kd], s uint8 [..., ceil(Kd/64), 2])."""
+    _need(x, torch.bfloat16, "x")
+    kd = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    x2 = x.reshape(-1, kd) if x.dim() != 2 else x
+    if x2.stride(-1) != 1:
+        raise ValueError("x must have unit stride along the last dim")
+    rows = x2.shape[0]
+    if q is None:
+        q = torch.empty(lead + (kd,), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty(lead + (_pairs(kd), 2), dtype=torch.uint8, device=x.device)
+    _need(q, torch.uint8, "q"); _need(s, torch.uint8, "s")
+    _need_contig(q, "q"); _need_contig(s, "s")
+    ld = x2.stride(0) if rows > 1 else kd
+    rc = load().mx_quantize(_ptr(x2), rows, kd, ld, _ptr(q), _ptr(s), _stream(stream))
+    _check(rc, "mx_quantize")
+    return q, s
+
+
+def route_workspace_size(T, k, E):
+    return int(load().moe_route_quant_workspace_size(T, k, E))
+
+
+def moe_route_quant(x, topk_ids, E, out=None, workspace=None, stream=None):
+    """Routing with fused MX activation quant.
+
+    Returns (xq [M,K] u8, xs [M,K/64,2] u8, sorted_row [M] i32,
+    expanded_row_idx [M] i32, group_list [E] i64 counts)."""
+    _need(x, torch.bfloat16, "x", 2); _need(topk_ids, torch.int32, "topk_ids", 2)
+    _need_contig(x, "x"); _need_contig(topk_ids, "topk_ids")
+    T, K = x.shape
+    k = topk_ids.shape[1]
+    M = T * k
+    dev = x.device
+    if out is None:
+        out = (torch.empty((M, K), dtype=torch.uint8, device=dev),
+               torch.empty((M, _pairs(K), 2), dtype=torch.uint8, device=dev),
+               torch.empty(M, dtype=torch.int32, device=dev),
+               torch.empty(M, dtype=torch.int32, device=dev),
+               torch.empty(E, dtype=torch.int64, device=dev))
+    xq, xs, sr, eri, gl = out
+    if workspace is None:
+        workspace = torch.empty(max(route_workspace_size(T, k, E), 256), dtype=torch.uint8, device=dev)
+    rc = load().moe_route_quant(_ptr(x), _ptr(topk_ids), T, K, k, E, _ptr(xq), _ptr(xs), _ptr(sr), _ptr(eri),
+                                _ptr(gl), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "moe_route_quant")
+    return xq, xs, sr, eri, gl
+
+
+def gmm_swiglu_mxquant(a, a_s, w13, w13_s, group_list, group_list_type=GROUP_COUNT, out=None,
+                       h_debug=False, stream=None):
+    """GEMM1 + SwiGLU + MX requant.  Returns (hq, hs) or (hq, hs, h) with h_debug."""
+    _need(a, torch.uint8, "a", 2); _need(w13, torch.uint8, "w13", 3)
+    _need(group_list, torch.int64, "group_list", 1)
+    for t, n in [(a, "a"), (a_s, "a_s"), (w13, "w13"), (w13_s, "w13_s"), (group_list, "group_list")]:
+        _need_contig(t, n)
+    M, K = a.shape
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    dev = a.device
+    if out is None:
+        out = (torch.empty((M, I), dtype=torch.uint8, device=dev),
+               torch.empty((M, _pairs(I), 2), dtype=torch.uint8, device=dev))
+    hq, hs = out
+    h = torch.empty((M, I), dtype=torch.float32, device=dev) if h_debug else None
+    rc = load().gmm_swiglu_mxquant(_ptr(a), _ptr(a_s), _ptr(w13), _ptr(w13_s), _ptr(group_list),
+                                   group_list_type, M, K, I, E, _ptr(hq), _ptr(hs), _ptr(h), _stream(stream))
+    _check(rc, "gmm_swiglu_mxquant")
+    return (hq, hs, h) if h_debug else (hq, hs)
+
+
+def gmm_mx(a, a_s, w, w_s, group_list, group_list_type=GROUP_COUNT, out=None, stream=None):
+    """Grouped MX GEMM, bf16 output [M, N]."""
+    _need(a, torch.uint8, "a", 2); _need(w, torch.uint8, "w", 3)
+    _need(group_list, torch.int64, "group_list", 1)
+    for t, n in [(a, "a"), (a_s, "a_s"), (w, "w"), (w_s, "w_s"), (group_list, "group_list")]:
+        _need_contig(t, n)
+    M, Kd = a.shape
+    E, N, _ = w.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    rc = load().gmm_mx(_ptr(a), _ptr(a_s), _ptr(w), _ptr(w_s), _ptr(group_list), group_list_type, M, N, Kd, E,
+                       _ptr(out), _stream(stream))
+    _check(rc, "gmm_mx")
+    return out
+
+
+def moe_finalize(y, topk_w, expanded_row_idx, out=None, stream=None):
+    """Weighted un-permute and sum: out [T, K] bf16."""
+    _need(y, torch.bfloat16, "y", 2); _need(topk_w, torch.float32, "topk_w", 2)
+    _need(expanded_row_idx, torch.int32, "expanded_row_idx")
+    for t, n in [(y, "y"), (topk_w, "topk_w"), (expanded_row_idx, "expanded_row_idx")]:
+        _need_contig(t, n)
+    M, K = y.shape
+    T, k = topk_w.shape
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.bfloat16, device=y.device)
+    rc = load().moe_finalize(_ptr(y), _ptr(topk_w), _ptr(expanded_row_idx), T, K, k, M, _ptr(out),
+                             _stream(stream))
+    _check(rc, "moe_finalize")
+    return out
+
+
+def forward_workspace_size(T, K, I, E, k):
+    return int(load().moe_mxfp8_forward_workspace_size(T, K, I, E, k))
+
+
+def forward_workspace(T, K, I, E, k, device="cuda"):
+    return torch.empty(max(forward_workspace_size(T, K, I, E, k), 256), dtype=torch.uint8, device=device)
+
+
+def moe_mxfp8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, workspace=None, stream=None):
+    """The whole layer.  x [T,K] bf16, topk_ids [T,k] i32, topk_w [T,k] f32,
+    w13 [E,2I,K] u8 + w13_s [E,2I,K/64,2], w2 [E,K,I] u8 + w2_s [E,K,I/64,2].
+    Returns out [T,K] bf16."""
+    _need(x, torch.bfloat16, "x", 2); _need(topk_ids, torch.int32, "topk_ids", 2)
+    _need(topk_w, torch.float32, "topk_w", 2); _need(w13, torch.uint8, "w13", 3); _need(w2, torch.uint8, "w2", 3)
+    for t, n in [(x, "x"), (topk_ids, "topk_ids"), (topk_w, "topk_w"), (w13, "w13"), (w13_s, "w13_s"),
+                 (w2, "w2"), (w2_s, "w2_s")]:
+        _need_contig(t, n)
+    T, K = x.shape
+    k = topk_ids.shape[1]
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = forward_workspace(T, K, I, E, k, x.device)
+    rc = load().moe_mxfp8_forward(_ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w13), _ptr(w13_s), _ptr(w2),
+                                  _ptr(w2_s), T, K, I, E, k, _ptr(out), _ptr(workspace), workspace.numel(),
+                                  _stream(stream))
+    _check(rc, "moe_mxfp8_forward")
+    return out
+
+
+def forward_intermediates(workspace, T, K, I, E, k):
+    """Views of the intermediates a forward call left in its workspace:
+    dict(xq, xs, sorted_row, expanded_row_idx, group_list, hq, hs, y)."""
+    offs = (ctypes.c_size_t * 8)()
+    _check(load().moe_mxfp8_forward_workspace_layout(T, K, I, E, k, offs), "workspace_layout")
+    M = T * k
+
+    def view(i, n, dtype):
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return workspace[offs[i]:offs[i] + nbytes].view(dtype)
+
+    return dict(
+        xq=view(0, M * K, torch.uint8).view(M, K),
+        xs=view(1, M * _pairs(K) * 2, torch.uint8).view(M, _pairs(K), 2),
+        sorted_row=view(2, M, torch.int32),
+        expanded_row_idx=view(3, M, torch.int32),
+        group_list=view(4, E, torch.int64),
+        hq=view(5, M * I, torch.uint8).view(M, I),
+        hs=view(6, M * _pairs(I) * 2, torch.uint8).view(M, _pairs(I), 2),
+        y=view(7, M * K, torch.bfloat16).view(M, K),
+    )

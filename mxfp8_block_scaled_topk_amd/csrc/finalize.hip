@@ -1,0 +1,98 @@
+// moe_finalize: out[t] = bf16( sum_j w[t,j] * y[expanded_row_idx[t*k+j]] ).
+//
+// One lane owns 8 consecutive output columns (16 bytes) of one token.  It
+// issues the gathers of all k source rows before accumulating, so k 16-byte
+// loads are in flight per lane; the sum runs in ascending j with every
+// product and add rounded to float32 (no fused multiply-add), which makes the
+// result independent of the launch shape.  HBM-bound: 2*k*K bytes read and
+// 2*K written per token, plus the k indices and weights.
+#include "common.h"
+
+namespace mxmoe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBatch = 8;   // source rows gathered before accumulating
+
+__global__ __launch_bounds__(kThreads) void finalize_kernel(
+    const uint16_t* __restrict__ y, const float* __restrict__ w, const int32_t* __restrict__ eri,
+    int64_t T, int64_t K, int k, int64_t M, uint16_t* __restrict__ out) {
+  const int64_t cpr = K / 8;                     // 16-byte chunks per row
+  const int64_t total = T * cpr;
+  for (int64_t it = blockIdx.x * (int64_t)kThreads + threadIdx.x; it < total;
+       it += (int64_t)gridDim.x * kThreads) {
+    const int64_t t = it / cpr;
+    const int64_t col = (it - t * cpr) * 8;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += kBatch) {
+      uint4 rows[kBatch];
+      float wt[kBatch];
+      bool ok[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int j = j0 + b;
+        ok[b] = false;
+        if (j < k) {
+          const int32_t p = eri[t * k + j];
+          wt[b] = w[t * k + j];
+          ok[b] = p >= 0 && p < M;
+          if (ok[b]) rows[b] = *reinterpret_cast<const uint4*>(y + (int64_t)p * K + col);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (!ok[b]) continue;
+        float v[8];
+        unpack_bf16x8(rows[b], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = __fadd_rn(acc[i], __fmul_rn(wt[b], v[i]));
+      }
+    }
+    uint4 o;
+    o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+    o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+    o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+    o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(out + t * K + col) = o;
+  }
+}
+
+}  // namespace
+
+int launch_finalize(const uint16_t* y, const float* w, const int32_t* eri, int64_t T, int64_t K,
+                    int64_t k, int64_t M, uint16_t* out, hipStream_t stream) {
+  const int64_t total = T * (K / 8);
+  if (total == 0) return MX_OK;
+  int64_t grid = (total + kThreads - 1) / kThreads;
+  const int64_t cap = (int64_t)num_cus() * 32;
+  if (grid > cap) grid = cap;
+  finalize_kernel<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(y, w, eri, T, K, (int)k, M, out);
+  return check_launch("moe_finalize");
+}
+
+int check_finalize_args(int64_t T, int64_t K, int64_t k, int64_t M) {
+  if (T < 0 || K <= 0 || k <= 0 || M < 0)
+    return fail(MX_ERR_INVALID_ARG, "moe_finalize: bad sizes T=%lld K=%lld k=%lld M=%lld", (long long)T,
+                (long long)K, (long long)k, (long long)M);
+  if (K % 8 != 0) return fail(MX_ERR_UNSUPPORTED, "moe_finalize: K=%lld is not a multiple of 8", (long long)K);
+  if (M >= (int64_t)1 << 31) return fail(MX_ERR_UNSUPPORTED, "moe_finalize: M >= 2^31");
+  return MX_OK;
+}
+
+}  // namespace mxmoe
+
+extern "C" int moe_finalize(const void* y_bf16, const float* topk_w, const int32_t* expanded_row_idx,
+                            int64_t T, int64_t K, int64_t k, int64_t M, void* out_bf16, void* stream) {
+  using namespace mxmoe;
+  int rc = check_finalize_args(T, K, k, M);
+  if (rc) return rc;
+  if (T > 0 && (!topk_w || !expanded_row_idx || !out_bf16 || (M > 0 && !y_bf16)))
+    return fail(MX_ERR_INVALID_ARG, "moe_finalize: null pointer");
+  if (reinterpret_cast<uintptr_t>(y_bf16) % 16 || reinterpret_cast<uintptr_t>(out_bf16) % 16)
+    return fail(MX_ERR_UNSUPPORTED, "moe_finalize: y and out must be 16-byte aligned");
+  return launch_finalize(static_cast<const uint16_t*>(y_bf16), topk_w, expanded_row_idx, T, K, k, M,
+                         static_cast<uint16_t*>(out_bf16), as_stream(stream));
+}

@@ -1,0 +1,97 @@
+// mx_quantize: bf16 rows -> e4m3 payload + pair-split e8m0 scales.
+//
+// One lane owns one 32-element block: it reads the block's 64 bytes, takes
+// the amax in registers, derives the e8m0 byte and converts the 32 values.
+// Consecutive lanes own consecutive blocks of a row, so loads and stores of a
+// wave are contiguous.  HBM-bound: 2 bytes in, 1 + 1/32 bytes out per element.
+#include "common.h"
+
+namespace mxmoe {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Fast path: kd % 32 == 0, ld % 8 == 0 (16-byte aligned rows).
+__global__ __launch_bounds__(kThreads) void mx_quantize_vec(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t kd, int64_t ld,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int64_t nb = kd / 32;
+  const int64_t s_stride = ((nb + 1) / 2) * 2;
+  const int64_t total = rows * nb;
+  for (int64_t blk = blockIdx.x * (int64_t)kThreads + threadIdx.x; blk < total;
+       blk += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = blk / nb, c = blk - r * nb;
+    const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + c * 32);
+    uint4 u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = src[i];
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack_bf16x8(u[i], v + 8 * i);
+    uint32_t w[8];
+    uint32_t sb = mx_block32(v, w);
+    uint4* dst = reinterpret_cast<uint4*>(q + r * kd + c * 32);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    s[r * s_stride + c] = static_cast<uint8_t>(sb);
+    if ((nb & 1) && c == nb - 1) s[r * s_stride + nb] = 0;
+  }
+}
+
+// General path: any kd (partial last block), any ld; element-wise accesses.
+__global__ __launch_bounds__(kThreads) void mx_quantize_any(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t kd, int64_t ld,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int64_t nb = (kd + 31) / 32;
+  const int64_t s_stride = ((nb + 1) / 2) * 2;
+  const int64_t total = rows * nb;
+  for (int64_t blk = blockIdx.x * (int64_t)kThreads + threadIdx.x; blk < total;
+       blk += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = blk / nb, c = blk - r * nb;
+    const int64_t k0 = c * 32;
+    const int n = static_cast<int>(kd - k0 < 32 ? kd - k0 : 32);
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = i < n ? bf16_to_f32(x[r * ld + k0 + i]) : 0.0f;
+    uint32_t w[8];
+    uint32_t sb = mx_block32(v, w);
+    for (int i = 0; i < n; ++i) q[r * kd + k0 + i] = static_cast<uint8_t>(w[i >> 2] >> (8 * (i & 3)));
+    s[r * s_stride + c] = static_cast<uint8_t>(sb);
+    if ((nb & 1) && c == nb - 1) s[r * s_stride + nb] = 0;
+  }
+}
+
+}  // namespace
+
+int launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t kd, int64_t ld,
+                       uint8_t* q, uint8_t* s, hipStream_t stream) {
+  const int64_t nb = (kd + 31) / 32;
+  const int64_t total = rows * nb;
+  if (total == 0) return MX_OK;
+  int64_t grid = (total + kThreads - 1) / kThreads;
+  const int64_t cap = (int64_t)num_cus() * 16;
+  if (grid > cap) grid = cap;
+  const bool vec = (kd % 32 == 0) && (ld % 8 == 0) &&
+                   (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(q) % 16 == 0);
+  if (vec)
+    mx_quantize_vec<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(x, rows, kd, ld, q, s);
+  else
+    mx_quantize_any<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(x, rows, kd, ld, q, s);
+  return check_launch("mx_quantize");
+}
+
+}  // namespace mxmoe
+
+extern "C" int mx_quantize(const void* x_bf16, int64_t rows, int64_t kd, int64_t ld,
+                           void* q_u8, void* s_u8, void* stream) {
+  using namespace mxmoe;
+  if (!x_bf16 || !q_u8 || !s_u8) return fail(MX_ERR_INVALID_ARG, "mx_quantize: null pointer");
+  if (rows < 0 || kd <= 0 || ld < kd)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize: bad sizes rows=%lld kd=%lld ld=%lld",
+                (long long)rows, (long long)kd, (long long)ld);
+  return launch_mx_quantize(static_cast<const uint16_t*>(x_bf16), rows, kd, ld,
+                            static_cast<uint8_t*>(q_u8), static_cast<uint8_t*>(s_u8),
+                            as_stream(stream));
+}

@@ -1,0 +1,264 @@
+// moe_route_quant: top-k routing with the MX activation quant fused in.
+//
+// The T*k assignments (flat index i = t*k + j) are cut into chunks of whole
+// tokens, at most 256 assignments each (one per thread).  Three launches:
+//
+//   route_hist           per chunk, per expert assignment counts (LDS atomics;
+//                        counts are order-free so atomics keep it exact)
+//   route_scan           one wave per expert: exclusive prefix of its counts
+//                        over the chunks, plus the expert's total (= group_list)
+//   route_scatter_quant  per chunk: the stable rank of every assignment among
+//                        the chunk's assignments to the same expert (wave
+//                        ballot match + per-wave counts in LDS), hence its row
+//                        p = offset[e] + prefix[e][chunk] + rank; writes both
+//                        maps; then MX-quantises each token of the chunk once,
+//                        in registers, and stores the payload and scales to
+//                        the token's k rows.
+//
+// The order inside an expert is the flat index order, so the permutation is
+// deterministic and equals a stable sort by expert.
+#include <algorithm>
+
+#include "common.h"
+
+namespace mxmoe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxE = 1024;
+
+__global__ __launch_bounds__(kThreads) void route_hist(const int32_t* __restrict__ ids, int64_t M,
+                                                       int k, int E, int tpc, int nchunks,
+                                                       int32_t* __restrict__ counts) {
+  __shared__ int hist[kMaxE];
+  for (int e = threadIdx.x; e < E; e += kThreads) hist[e] = 0;
+  __syncthreads();
+  const int c = blockIdx.x;
+  const int64_t a = (int64_t)c * tpc * k + threadIdx.x;
+  if ((int)threadIdx.x < tpc * k && a < M) {
+    const int e = ids[a];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) counts[(int64_t)e * nchunks + c] = hist[e];
+}
+
+// counts [E][nchunks] -> exclusive prefix over chunks (in place); totals[e].
+__global__ __launch_bounds__(kThreads) void route_scan(int32_t* __restrict__ counts, int nchunks, int E,
+                                                       int32_t* __restrict__ totals,
+                                                       int64_t* __restrict__ group_list) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * (kThreads / 64) + wave;
+  if (e >= E) return;  // uniform per wave
+  int32_t* row = counts + (int64_t)e * nchunks;
+  int run = 0;
+  for (int base = 0; base < nchunks; base += 64) {
+    const int i = base + lane;
+    const int v = i < nchunks ? row[i] : 0;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (i < nchunks) row[i] = run + x - v;
+    run += __shfl(x, 63);
+  }
+  if (lane == 0) {
+    totals[e] = run;
+    group_list[e] = run;
+  }
+}
+
+// Exclusive scan of v[0..n) (n <= 1024) into out[0..n) by one 256-thread block.
+__device__ void block_exclusive_scan(const int32_t* __restrict__ v, int n, int* out, int* s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int loc[4];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    loc[i] = e < n ? v[e] : 0;
+    sum += loc[i];
+  }
+  int x = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wsum[wave] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += s_wsum[w];
+  int run = base + x - sum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    if (e < n) out[e] = run;
+    run += loc[i];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void route_scatter_quant(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, int64_t T, int64_t K, int k,
+    int E, int nbits, int tpc, int nchunks, const int32_t* __restrict__ prefix,
+    const int32_t* __restrict__ totals, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+    int32_t* __restrict__ sorted_row, int32_t* __restrict__ eri) {
+  __shared__ int s_off[kMaxE];
+  __shared__ int s_wcnt[kThreads / 64][kMaxE];
+  __shared__ int s_pos[kThreads];
+  __shared__ int s_wsum[kThreads / 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x;
+  for (int w = 0; w < kThreads / 64; ++w)
+    for (int e = tid; e < E; e += kThreads) s_wcnt[w][e] = 0;
+  block_exclusive_scan(totals, E, s_off, s_wsum);
+  __syncthreads();
+
+  // ---- stable rank of each assignment within the chunk -------------------
+  const int64_t M = T * k;
+  const int64_t a0 = (int64_t)c * tpc * k;
+  const int na = (int)std::min<int64_t>((int64_t)tpc * k, M - a0);
+  const int64_t a = a0 + tid;
+  int e = 0;
+  bool valid = false;
+  if (tid < na) {
+    e = ids[a];
+    valid = e >= 0 && e < E;
+  }
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t ones = __ballot(bit);
+    same &= bit ? ones : ~ones;
+  }
+  int rank = __popcll(same & ((1ull << lane) - 1ull));
+  if (valid && rank == 0) s_wcnt[wave][e] = __popcll(same);
+  __syncthreads();
+  int pos = -1;
+  if (valid) {
+    for (int w = 0; w < wave; ++w) rank += s_wcnt[w][e];
+    pos = s_off[e] + prefix[(int64_t)e * nchunks + c] + rank;
+    sorted_row[pos] = (int32_t)a;
+  }
+  if (tid < na) eri[a] = pos;
+  s_pos[tid] = pos;
+  __syncthreads();
+
+  // ---- MX quant of the chunk's tokens, stored to each token's k rows ------
+  const int64_t nb = K / 32;
+  const int64_t s_stride = ((nb + 1) / 2) * 2;
+  const int64_t t0 = (int64_t)c * tpc;
+  const int ntok = (int)std::min<int64_t>((int64_t)tpc, T - t0);
+  const int64_t items = (int64_t)ntok * nb;
+  for (int64_t it = tid; it < items; it += kThreads) {
+    const int tl = (int)(it / nb);
+    const int64_t b = it - (int64_t)tl * nb;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (t0 + tl) * K + b * 32);
+    uint4 u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = src[i];
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack_bf16x8(u[i], v + 8 * i);
+    uint32_t w[8];
+    const uint32_t sb = mx_block32(v, w);
+    const uint4 q0 = make_uint4(w[0], w[1], w[2], w[3]);
+    const uint4 q1 = make_uint4(w[4], w[5], w[6], w[7]);
+    for (int j = 0; j < k; ++j) {
+      const int p = s_pos[tl * k + j];
+      if (p < 0) continue;
+      uint4* dst = reinterpret_cast<uint4*>(xq + (int64_t)p * K + b * 32);
+      dst[0] = q0;
+      dst[1] = q1;
+      xs[(int64_t)p * s_stride + b] = static_cast<uint8_t>(sb);
+      if ((nb & 1) && b == nb - 1) xs[(int64_t)p * s_stride + nb] = 0;
+    }
+  }
+}
+
+__global__ void zero_i64(int64_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+inline int64_t tokens_per_chunk(int64_t k) { return std::max<int64_t>(1, kThreads / k); }
+inline int64_t num_chunks(int64_t T, int64_t k) {
+  const int64_t tpc = tokens_per_chunk(k);
+  return (T + tpc - 1) / tpc;
+}
+
+}  // namespace
+
+size_t route_workspace_bytes(int64_t T, int64_t k, int64_t E) {
+  const int64_t nch = num_chunks(T, k);
+  return align_up((size_t)(E * nch) * 4, 256) + align_up((size_t)E * 4, 256);
+}
+
+int check_route_args(int64_t T, int64_t K, int64_t k, int64_t E) {
+  if (T < 0 || K <= 0 || k <= 0 || E <= 0)
+    return fail(MX_ERR_INVALID_ARG, "moe_route_quant: bad sizes T=%lld K=%lld k=%lld E=%lld",
+                (long long)T, (long long)K, (long long)k, (long long)E);
+  if (k > E) return fail(MX_ERR_INVALID_ARG, "moe_route_quant: k=%lld > E=%lld", (long long)k, (long long)E);
+  if (K % 32 != 0) return fail(MX_ERR_UNSUPPORTED, "moe_route_quant: K=%lld is not a multiple of 32", (long long)K);
+  if (k > kThreads) return fail(MX_ERR_UNSUPPORTED, "moe_route_quant: k=%lld > %d", (long long)k, kThreads);
+  if (E > kMaxE) return fail(MX_ERR_UNSUPPORTED, "moe_route_quant: E=%lld > %d", (long long)E, kMaxE);
+  if (T * k >= (int64_t)1 << 31) return fail(MX_ERR_UNSUPPORTED, "moe_route_quant: T*k >= 2^31");
+  return MX_OK;
+}
+
+int launch_route_quant(const uint16_t* x, const int32_t* ids, int64_t T, int64_t K, int64_t k,
+                       int64_t E, uint8_t* xq, uint8_t* xs, int32_t* sorted_row, int32_t* eri,
+                       int64_t* group_list, void* ws, hipStream_t stream) {
+  const int64_t tpc = tokens_per_chunk(k);
+  const int64_t nch = num_chunks(T, k);
+  int32_t* counts = static_cast<int32_t*>(ws);
+  int32_t* totals = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up((size_t)(E * nch) * 4, 256));
+  if (T == 0) {
+    zero_i64<<<dim3((unsigned)((E + 255) / 256)), dim3(256), 0, stream>>>(group_list, (int)E);
+    return check_launch("moe_route_quant(zero)");
+  }
+  int nbits = 0;
+  while ((1ll << nbits) < E) ++nbits;
+  route_hist<<<dim3((unsigned)nch), dim3(kThreads), 0, stream>>>(ids, T * k, (int)k, (int)E, (int)tpc,
+                                                                   (int)nch, counts);
+  int rc = check_launch("route_hist");
+  if (rc) return rc;
+  route_scan<<<dim3((unsigned)((E + 3) / 4)), dim3(kThreads), 0, stream>>>(counts, (int)nch, (int)E, totals,
+                                                                           group_list);
+  rc = check_launch("route_scan");
+  if (rc) return rc;
+  route_scatter_quant<<<dim3((unsigned)nch), dim3(kThreads), 0, stream>>>(
+      x, ids, T, K, (int)k, (int)E, nbits, (int)tpc, (int)nch, counts, totals, xq, xs, sorted_row, eri);
+  return check_launch("route_scatter_quant");
+}
+
+}  // namespace mxmoe
+
+extern "C" size_t moe_route_quant_workspace_size(int64_t T, int64_t k, int64_t E) {
+  if (T < 0 || k <= 0 || E <= 0) return 0;
+  return mxmoe::route_workspace_bytes(T, k, E);
+}
+
+extern "C" int moe_route_quant(const void* x_bf16, const int32_t* topk_ids, int64_t T, int64_t K,
+                               int64_t k, int64_t E, void* xq_u8, void* xs_u8, int32_t* sorted_row,
+                               int32_t* expanded_row_idx, int64_t* group_list, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  using namespace mxmoe;
+  int rc = check_route_args(T, K, k, E);
+  if (rc) return rc;
+  if (!group_list || !workspace) return fail(MX_ERR_INVALID_ARG, "moe_route_quant: null pointer");
+  if (T > 0 && (!x_bf16 || !topk_ids || !xq_u8 || !xs_u8 || !sorted_row || !expanded_row_idx))
+    return fail(MX_ERR_INVALID_ARG, "moe_route_quant: null pointer");
+  const size_t need = route_workspace_bytes(T, k, E);
+  if (ws_bytes < need)
+    return fail(MX_ERR_WORKSPACE, "moe_route_quant: workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(x_bf16) % 16 || reinterpret_cast<uintptr_t>(xq_u8) % 16)
+    return fail(MX_ERR_UNSUPPORTED, "moe_route_quant: x and xq must be 16-byte aligned");
+  return launch_route_quant(static_cast<const uint16_t*>(x_bf16), topk_ids, T, K, k, E,
+                            static_cast<uint8_t*>(xq_u8), static_cast<uint8_t*>(xs_u8), sorted_row,
+                            expanded_row_idx, group_list, workspace, as_stream(stream));
+}

@@ -1,0 +1,145 @@
+"""Helpers shared by the GPU parity tests (host <-> device marshalling and
+the comparison rules).  Imported only by tests marked ``gpu``."""
+
+import os
+import sys
+
+import numpy as np
+import torch
+
+from oracle import mx_ref
+
+
+def say(msg):
+    """Name the case before each GPU step, flushed, so a failing run says which.
+    With MXMOE_CASE_LOG set, the line is also appended to that file (passing
+    tests' measured errors are otherwise not shown)."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+    path = os.environ.get("MXMOE_CASE_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(msg + "\n")
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def bf16_dev(bits):
+    """uint16 bf16 bit patterns (NumPy) -> torch.bfloat16 on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev())
+
+
+def bf16_host(t):
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def u8_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev())
+
+
+def i32_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev())
+
+
+def i64_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).to(dev())
+
+
+def f32_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def row_rel_err(got, ref):
+    """Per-row max|got - ref| / max|ref| (the 2e-2 output rule); a row whose
+    reference is all zero must be all zero.  Returns the per-row errors."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape
+    num = np.abs(got - ref).max(axis=1)
+    den = np.abs(ref).max(axis=1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
+def bf16_rows_rel_err(got_bits, ref_bits):
+    return row_rel_err(mx_ref.bf16_to_f64(got_bits), mx_ref.bf16_to_f64(ref_bits))
+
+
+def quantize_experts_ref(w_bits):
+    """Oracle MX quantisation of bf16 expert weights [E, N, Kd] (host)."""
+    E, N, Kd = w_bits.shape
+    q, s = mx_ref.mx_quantize_ref(mx_ref.bf16_to_f64(w_bits.reshape(E * N, Kd)))
+    return q.reshape(E, N, Kd), s.reshape(E, N, -1, 2)
+
+
+class LazyExpertQuant:
+    """Per-expert oracle quantisation on first use (full-size workloads touch
+    only the experts of the sampled tokens)."""
+
+    def __init__(self, w_bits):
+        self.w = w_bits
+        self.shape = w_bits.shape
+        self.cache = {}
+
+    def get(self, e):
+        if e not in self.cache:
+            q, s = mx_ref.mx_quantize_ref(mx_ref.bf16_to_f64(self.w[e]))
+            self.cache[e] = (q, s)
+        return self.cache[e]
+
+
+class FixedExperts:
+    """Already-quantised expert weights with the LazyExpertQuant interface."""
+
+    def __init__(self, q, s):
+        self.q, self.s = q, s
+        self.shape = q.shape
+
+    def get(self, e):
+        return self.q[e], self.s[e]
+
+
+def guard_alloc(n, dtype, guard=4096, fill=0xA5):
+    """A tensor of n elements with guard bands either side filled with `fill`."""
+    esize = torch.empty((), dtype=dtype).element_size()
+    gb = guard // esize
+    raw = torch.full(((n + 2 * gb) * esize,), fill, dtype=torch.uint8, device=dev())
+    return raw, raw[guard:guard + n * esize].view(dtype)
+
+
+def guards_intact(raw, n_bytes, guard=4096, fill=0xA5):
+    h = raw.cpu().numpy()
+    return bool(np.all(h[:guard] == fill) and np.all(h[guard + n_bytes:] == fill))
+
+
+def explain_hq_mismatches(hq, hs, hq_ref, h_ref, rtol=1e-3):
+    """GEMM1's requant bytes may differ from the oracle's where the kernel's
+    float32 h (MFMA accumulation) and the oracle's (float64 accumulation)
+    round differently: near an e4m3 rounding midpoint, across a power-of-two
+    block amax, or on elements much smaller than their row, whose absolute
+    error is set by the row.  A GPU byte is accepted when it is the correct
+    rounding of some h' within rtol * max|h_ref row| of the oracle's h:
+        |deq(gpu) - h_ref| <= rtol * rowmax + half the e4m3 spacing at deq(gpu)
+    (the spacing in the block's own scale), or the byte is the saturated
+    code +-448 * 2^s and h_ref lies at or beyond that value.  Returns (number of bytes that
+    differ from the oracle's, number not accepted)."""
+    M, I = hq.shape
+    nb = I // 32
+    sb = hs.reshape(M, -1)[:, :nb].astype(np.int64)
+    scale = np.repeat(np.exp2(sb - 127.0), 32, axis=1)
+    q = hq.astype(np.int64)
+    deq = mx_ref.e4m3_decode(q) * scale
+    ef = (q >> 3) & 0xF
+    spacing = np.where(ef == 0, 2.0 ** -9, np.exp2(ef - 10.0)) * scale
+    h = np.asarray(h_ref, np.float64)
+    atol = rtol * np.abs(h).max(axis=1, keepdims=True)
+    ok = np.abs(deq - h) <= atol + 0.5 * spacing * (1 + 1e-9)
+    # saturation: the largest code stands for every h' at or beyond 448 * 2^s
+    sat = ((q & 0x7F) == 0x7E) & (np.sign(deq) * h >= np.abs(deq) - atol)
+    ok |= sat
+    return int(np.sum(hq != hq_ref)), int(np.sum(~ok))

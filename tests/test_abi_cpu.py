@@ -1,0 +1,128 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/mxmoe.h declares, and rejects bad arguments on the host with the
+documented status codes before anything is enqueued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_block_scaled_topk_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxmoe.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = ctypes.c_void_p(0x1000)     # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mx.lib_path()):
+        pytest.fail("libmxmoe.so is not built (run python -m mxfp8_block_scaled_topk_amd.build)")
+    return mx.load()
+
+
+def test_header_declares_the_six_entry_points():
+    names = declared_functions()
+    for n in ["mx_quantize", "moe_route_quant", "gmm_swiglu_mxquant", "gmm_mx", "moe_finalize",
+              "moe_mxfp8_forward", "mx_last_error"]:
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in mxmoe.h but not exported"
+
+
+def test_workspace_queries(lib):
+    assert mx.route_workspace_size(16384, 8, 128) > 0
+    ws = mx.forward_workspace_size(16384, 2048, 768, 128, 8)
+    M = 16384 * 8
+    assert ws >= M * 2048 + M * 768 + M * 2048 * 2       # xq + hq + y at least
+    assert mx.forward_workspace_size(-1, 2048, 768, 128, 8) == 0
+    offs = (ctypes.c_size_t * 8)()
+    assert lib.moe_mxfp8_forward_workspace_layout(64, 256, 128, 8, 2, offs) == OK
+    assert list(offs) == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lib.moe_mxfp8_forward_workspace_layout(64, 256, 128, 8, 2, None) == INVALID
+
+
+def test_mx_quantize_validation(lib):
+    assert lib.mx_quantize(None, 4, 64, 64, FAKE, FAKE, None) == INVALID
+    assert "null" in mx.last_error()
+    assert lib.mx_quantize(FAKE, 4, 0, 64, FAKE, FAKE, None) == INVALID
+    assert lib.mx_quantize(FAKE, 4, 64, 32, FAKE, FAKE, None) == INVALID   # ld < kd
+    assert lib.mx_quantize(FAKE, -1, 64, 64, FAKE, FAKE, None) == INVALID
+
+
+def test_route_validation(lib):
+    f = lib.moe_route_quant
+    args = lambda T, K, k, E, ws=1 << 20: f(FAKE, FAKE, T, K, k, E, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+    assert args(64, 256, 9, 8) == INVALID          # k > E
+    assert args(64, 256, 0, 8) == INVALID
+    assert args(64, 100, 2, 8) == UNSUPPORTED      # K % 32
+    assert args(64, 256, 2, 2048) == UNSUPPORTED   # E > 1024
+    assert args(64, 256, 300, 400) == UNSUPPORTED  # k > 256
+    assert args(64, 256, 2, 8, ws=0) == WORKSPACE
+    assert "workspace" in mx.last_error()
+    assert f(None, FAKE, 64, 256, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
+
+
+def test_gmm_validation(lib):
+    g = lib.gmm_mx
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, 128, 128, 4, FAKE, None) == INVALID   # bad type
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 100, 128, 4, FAKE, None) == UNSUPPORTED  # N % 128
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 96, 4, FAKE, None) == UNSUPPORTED   # Kd % 128
+    assert g(FAKE, FAKE, FAKE, FAKE, None, 1, 16, 128, 128, 4, FAKE, None) == INVALID     # null group list
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 128, 0, FAKE, None) == INVALID     # E = 0
+    s = lib.gmm_swiglu_mxquant
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 96, 4, FAKE, FAKE, None, None) == UNSUPPORTED  # I % 64
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 16, 128, 128, 4, FAKE, FAKE, None, None) == INVALID
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 128, 4, None, FAKE, None, None) == INVALID
+
+
+def test_finalize_validation(lib):
+    f = lib.moe_finalize
+    assert f(FAKE, FAKE, FAKE, 4, 100, 2, 8, FAKE, None) == UNSUPPORTED   # K % 8
+    assert f(FAKE, FAKE, FAKE, 4, 128, 0, 8, FAKE, None) == INVALID
+    assert f(FAKE, None, FAKE, 4, 128, 2, 8, FAKE, None) == INVALID
+
+
+def test_forward_validation(lib):
+    f = lib.moe_mxfp8_forward
+    call = lambda T, K, I, E, k, ws=1 << 30: f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, K, I, E, k, FAKE, FAKE,
+                                               ws, None)
+    assert call(64, 256, 96, 8, 2) == UNSUPPORTED      # I % 128
+    assert call(64, 200, 128, 8, 2) == UNSUPPORTED     # K % 32
+    assert call(64, 256, 128, 8, 9) == INVALID         # k > E
+    assert call(64, 256, 128, 8, 2, ws=16) == WORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 256, 128, 8, 2, FAKE, None, 1 << 30, None) == INVALID
+
+
+def test_error_text_is_thread_local(lib):
+    import threading
+    lib.mx_quantize(None, 4, 64, 64, FAKE, FAKE, None)
+    seen = {}
+
+    def other():
+        seen["msg"] = mx.last_error()
+
+    t = threading.Thread(target=other)
+    t.start(); t.join()
+    assert seen["msg"] == "no error"
+    assert "null" in mx.last_error()
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mx, "_LIB", None)
+    monkeypatch.setattr(mx, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(mx.MxError):
+        mx.load()

@@ -1,0 +1,353 @@
+"""Per-kernel parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: bit-exact for quantised bytes, scales and routing indices; bf16
+outputs within a per-row max relative error of 2e-2; GEMM1's h within 1e-3
+and its requant bytes bit-exact given the kernel's own h.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_topk_amd as mx
+from gpu_util import (bf16_dev, bf16_host, bf16_rows_rel_err, explain_hq_mismatches, f32_dev, guard_alloc,
+                      guards_intact, host, i32_dev, i64_dev, row_rel_err, say, u8_dev)
+from oracle import moe_ref, mx_ref
+from workloads import to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+RNG = np.random.default_rng(2024)
+TOL = 2e-2
+
+
+def _rand_bf16(shape, scale_spread=0):
+    x = RNG.standard_normal(shape).astype(np.float32)
+    if scale_spread:
+        x *= np.exp2(RNG.integers(-scale_spread, scale_spread, shape[:-1] + (1,))).astype(np.float32)
+    return to_bf16_bits(x)
+
+
+def _adversarial_rows():
+    """Blocks of 32 built to hit every branch of the quantiser."""
+    rows = []
+    z = np.zeros(32, np.float32)
+    rows.append(z)                                            # all zero
+    rows.append(-z)                                           # all -0
+    rows.append(np.full(32, 1e-40, np.float32))               # subnormal block
+    t = np.zeros(32, np.float32); t[0] = 256.0                # s = 0, exact ties below
+    t[1:9] = [1.0625, 1.1875, -1.0625, 2.125, 0.0029296875, -0.0029296875, 448.0, 464.0]
+    rows.append(t)
+    sat = np.full(32, 1.0, np.float32); sat[0] = 1.99; sat[1] = -1.99   # top element saturates
+    rows.append(sat)
+    rows.append(np.full(32, 3.0e38, np.float32))              # largest scale
+    tiny = np.full(32, 2.0 ** -126, np.float32); tiny[3] = -(2.0 ** -120)
+    rows.append(tiny)
+    mixed = (RNG.standard_normal(32) * np.exp2(RNG.integers(-40, 40, 32))).astype(np.float32)
+    rows.append(mixed)
+    return to_bf16_bits(np.concatenate(rows).reshape(1, -1))
+
+
+def _all_finite_bf16():
+    b = np.arange(65536, dtype=np.uint32)
+    f = (b << 16).view(np.float32)
+    bits = b[np.isfinite(f)].astype(np.uint16)
+    RNG.shuffle(bits)
+    n = (bits.size // 64) * 64
+    return bits[:n].reshape(-1, 64)
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (7, 64), (33, 2048), (5, 4304), (3, 40), (130, 768), (2, 8)])
+def test_mx_quantize_bitexact(shape):
+    say(f"mx_quantize shape={shape}")
+    x = _rand_bf16(shape, scale_spread=30)
+    q, s = mx.mx_quantize(bf16_dev(x))
+    torch.cuda.synchronize()
+    qr, sr = mx_ref.mx_quantize_ref(mx_ref.bf16_to_f64(x))
+    assert np.array_equal(host(q), qr)
+    assert np.array_equal(host(s), sr)
+
+
+def test_mx_quantize_adversarial_and_all_bf16():
+    for name, x in [("adversarial", _adversarial_rows()), ("all-bf16", _all_finite_bf16())]:
+        say(f"mx_quantize {name} {x.shape}")
+        q, s = mx.mx_quantize(bf16_dev(x))
+        torch.cuda.synchronize()
+        qr, sr = mx_ref.mx_quantize_ref(mx_ref.bf16_to_f64(x))
+        assert np.array_equal(host(q), qr), name
+        assert np.array_equal(host(s), sr), name
+
+
+def test_mx_quantize_strided_rows_and_3d():
+    say("mx_quantize strided rows")
+    wide = _rand_bf16((9, 512), scale_spread=8)
+    xd = bf16_dev(wide)[:, 128:384]                     # row stride 512, 256 columns
+    q, s = mx.mx_quantize(xd)
+    torch.cuda.synchronize()
+    qr, sr = mx_ref.mx_quantize_ref(mx_ref.bf16_to_f64(wide[:, 128:384]))
+    assert np.array_equal(host(q), qr) and np.array_equal(host(s), sr)
+    say("mx_quantize 3-D expert weights")
+    w = _rand_bf16((3, 64, 256))
+    q, s = mx.mx_quantize(bf16_dev(w))
+    torch.cuda.synchronize()
+    qr, sr = mx_ref.mx_quantize_ref(mx_ref.bf16_to_f64(w.reshape(-1, 256)))
+    assert q.shape == (3, 64, 256) and s.shape == (3, 64, 4, 2)
+    assert np.array_equal(host(q).reshape(-1, 256), qr) and np.array_equal(host(s).reshape(-1, 4, 2), sr)
+
+
+def test_mx_quantize_guard_bands():
+    say("mx_quantize guard bands")
+    x = _rand_bf16((17, 96))
+    rawq, q = guard_alloc(17 * 96, torch.uint8)
+    raws, s = guard_alloc(17 * 2 * 2, torch.uint8)
+    mx.mx_quantize(bf16_dev(x), q=q.view(17, 96), s=s.view(17, 2, 2))
+    torch.cuda.synchronize()
+    assert guards_intact(rawq, 17 * 96) and guards_intact(raws, 17 * 4)
+    qr, sr = mx_ref.mx_quantize_ref(mx_ref.bf16_to_f64(x))
+    assert np.array_equal(host(q).reshape(17, 96), qr) and np.array_equal(host(s).reshape(17, 2, 2), sr)
+
+
+# --------------------------------------------------------------------------
+# routing
+# --------------------------------------------------------------------------
+
+def _distinct_ids(T, k, E, p=None):
+    return np.stack([RNG.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+
+
+ROUTE_CASES = {
+    "small": (40, 256, 4, 12, None),
+    "ragged-many-chunks": (301, 512, 8, 64, None),
+    "k1": (257, 128, 1, 5, None),
+    "one-hot-expert": (200, 256, 4, 16, "hot"),
+    "sparse-experts": (100, 96, 2, 128, "sparse"),
+    "E1": (33, 64, 1, 1, None),
+    "k-eq-E": (50, 64, 6, 6, None),
+    "big-k": (70, 64, 32, 40, None),
+}
+
+
+def _route_ids(T, k, E, kind):
+    if kind == "hot":
+        ids = _distinct_ids(T, k - 1, E - 1) + 1
+        return np.concatenate([np.zeros((T, 1), np.int32), ids], axis=1)     # every token picks expert 0
+    if kind == "sparse":
+        used = RNG.choice(E, size=5, replace=False)
+        return np.stack([RNG.choice(used, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    return _distinct_ids(T, k, E)
+
+
+@pytest.mark.parametrize("name", list(ROUTE_CASES))
+def test_route_quant_bitexact(name):
+    T, K, k, E, kind = ROUTE_CASES[name]
+    say(f"moe_route_quant {name} T={T} K={K} k={k} E={E}")
+    x = _rand_bf16((T, K), scale_spread=10)
+    ids = _route_ids(T, k, E, kind)
+    xq, xs, sr, eri, gl = mx.moe_route_quant(bf16_dev(x), i32_dev(ids), E)
+    torch.cuda.synchronize()
+    rq, rs, rsr, reri, rc = moe_ref.route_quant_ref(x, ids, E)
+    assert np.array_equal(host(gl), rc)
+    assert np.array_equal(host(sr), rsr)
+    assert np.array_equal(host(eri), reri)
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(xs), rs)
+
+
+def test_route_quant_empty_batch():
+    say("moe_route_quant T=0")
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    gl = torch.full((8,), 7, dtype=torch.int64, device="cuda")
+    out = (torch.empty((0, 128), dtype=torch.uint8, device="cuda"),
+           torch.empty((0, 2, 2), dtype=torch.uint8, device="cuda"),
+           torch.empty(0, dtype=torch.int32, device="cuda"), torch.empty(0, dtype=torch.int32, device="cuda"), gl)
+    mx.moe_route_quant(x, ids, 8, out=out)
+    torch.cuda.synchronize()
+    assert host(gl).tolist() == [0] * 8
+
+
+def test_route_quant_invalid_ids_are_dropped():
+    T, K, k, E = 64, 128, 4, 10
+    say("moe_route_quant invalid ids")
+    x = _rand_bf16((T, K))
+    ids = _distinct_ids(T, k, E)
+    ids[3, 1] = -1
+    ids[10, 0] = E
+    ids[50, 3] = 1 << 20
+    xq, xs, sr, eri, gl = mx.moe_route_quant(bf16_dev(x), i32_dev(ids), E)
+    torch.cuda.synchronize()
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    assert np.array_equal(host(gl), np.bincount(flat[valid], minlength=E))
+    order = np.flatnonzero(valid)[np.argsort(flat[valid], kind="stable")]
+    nv = order.size
+    assert np.array_equal(host(sr)[:nv], order)
+    e = host(eri)
+    assert np.all(e[~valid] == -1)
+    assert np.array_equal(e[order], np.arange(nv))
+    qt, st = mx_ref.mx_quantize_ref(mx_ref.bf16_to_f64(x))
+    assert np.array_equal(host(xq)[:nv], qt[order // k])
+    assert np.array_equal(host(xs)[:nv], st[order // k])
+
+
+# --------------------------------------------------------------------------
+# grouped GEMMs
+# --------------------------------------------------------------------------
+
+def _mx_operands(M, Kd, E, N, spread=4):
+    a = RNG.standard_normal((M, Kd)) * np.exp2(RNG.integers(-spread, spread, (M, 1)))
+    w = RNG.standard_normal((E * N, Kd)) * 0.05 * np.exp2(RNG.integers(-spread, spread, (E * N, 1)))
+    aq, as_ = mx_ref.mx_quantize_ref(a)
+    wq, ws = mx_ref.mx_quantize_ref(w)
+    return aq, as_, wq.reshape(E, N, Kd), ws.reshape(E, N, -1, 2)
+
+
+GMM_CASES = {
+    "ragged": ([0, 1, 127, 128, 129, 300, 0, 5], 256, 256),
+    "single-expert": ([515], 384, 128),
+    "tiny-rows": ([1, 1, 1, 2], 128, 384),
+    "wide-k": ([64, 200], 1024, 128),
+}
+
+
+@pytest.mark.parametrize("name", list(GMM_CASES))
+@pytest.mark.parametrize("gl_type", [1, 0])
+def test_gmm_mx_parity(name, gl_type):
+    counts, Kd, N = GMM_CASES[name]
+    counts = np.array(counts, np.int64)
+    M, E = int(counts.sum()), len(counts)
+    say(f"gmm_mx {name} gl_type={gl_type} M={M} Kd={Kd} N={N} E={E}")
+    aq, as_, wq, ws = _mx_operands(M, Kd, E, N)
+    gl = counts if gl_type == 1 else np.cumsum(counts)
+    y = mx.gmm_mx(u8_dev(aq), u8_dev(as_), u8_dev(wq), u8_dev(ws), i64_dev(gl), gl_type)
+    torch.cuda.synchronize()
+    ref = moe_ref.gmm_mx_ref(aq, as_, wq, ws, gl, gl_type)
+    err = bf16_rows_rel_err(bf16_host(y), ref)
+    say(f"  max row rel err {err.max():.3g}")
+    assert err.max() <= TOL
+
+
+def test_gmm_mx_exact_cases():
+    say("gmm_mx all-ones and single-nonzero")
+    M, K, N, E = 300, 256, 128, 3
+    aq = np.full((M, K), 0x38, np.uint8)
+    as_ = np.full((M, K // 64, 2), 127, np.uint8)
+    wq = np.full((E, N, K), 0x38, np.uint8)
+    ws = np.full((E, N, K // 64, 2), 127, np.uint8)
+    y = mx.gmm_mx(u8_dev(aq), u8_dev(as_), u8_dev(wq), u8_dev(ws), i64_dev([100, 0, 200]), 1)
+    torch.cuda.synchronize()
+    assert np.all(mx_ref.bf16_to_f64(bf16_host(y)) == K)
+    aq = np.zeros((M, K), np.uint8)
+    aq[np.arange(M), np.arange(M) % K] = 0x40          # 2.0 at a moving k
+    as_ = np.full((M, K // 64, 2), 127, np.uint8)
+    as_[:, 0, 0] = 129
+    wq = np.zeros((E, N, K), np.uint8)
+    wq[:, :, :] = 0xB8                                 # -1.0 everywhere
+    y = mx.gmm_mx(u8_dev(aq), u8_dev(as_), u8_dev(wq), u8_dev(ws), i64_dev([100, 0, 200]), 1)
+    torch.cuda.synchronize()
+    ref = mx_ref.bf16_to_f64(moe_ref.gmm_mx_ref(aq, as_, wq, ws, np.array([100, 0, 200]), 1))
+    assert np.array_equal(mx_ref.bf16_to_f64(bf16_host(y)), ref)
+
+
+def test_gmm_mx_guard_bands_and_untouched_rows():
+    counts = np.array([0, 129, 0, 70], np.int64)
+    M, Kd, N, E = 250, 128, 128, 4                     # 51 rows owned by no expert
+    say("gmm_mx guard bands")
+    aq, as_, wq, ws = _mx_operands(M, Kd, E, N)
+    raw, y = guard_alloc(M * N, torch.bfloat16, fill=0x5A)
+    mx.gmm_mx(u8_dev(aq), u8_dev(as_), u8_dev(wq), u8_dev(ws), i64_dev(counts), 1, out=y.view(M, N))
+    torch.cuda.synchronize()
+    assert guards_intact(raw, M * N * 2, fill=0x5A)
+    yh = bf16_host(y.view(M, N))
+    assert np.all(yh[199:] == 0x5A5A)                  # rows past the last expert untouched
+
+
+GMM1_CASES = {
+    "ragged": ([3, 0, 128, 129, 1, 260], 256, 128),
+    "wide-i": ([70, 150], 128, 384),
+    "single": ([1], 512, 64),
+}
+
+
+@pytest.mark.parametrize("name", list(GMM1_CASES))
+def test_gmm_swiglu_mxquant_parity(name):
+    counts, K, I = GMM1_CASES[name]
+    counts = np.array(counts, np.int64)
+    M, E = int(counts.sum()), len(counts)
+    say(f"gmm_swiglu_mxquant {name} M={M} K={K} I={I} E={E}")
+    aq, as_, wq, ws = _mx_operands(M, K, E, 2 * I)
+    hq, hs, h = mx.gmm_swiglu_mxquant(u8_dev(aq), u8_dev(as_), u8_dev(wq), u8_dev(ws), i64_dev(counts), 1,
+                                      h_debug=True)
+    torch.cuda.synchronize()
+    rq, rs, rh = moe_ref.gmm_swiglu_mxquant_ref(aq, as_, wq, ws, counts, 1, I)
+    hk = host(h)
+    herr = row_rel_err(hk, rh)
+    say(f"  h max row rel err {herr.max():.3g}")
+    assert herr.max() <= 1e-3
+    # requant bytes are exact given the kernel's own h
+    kq, ks = mx_ref.mx_quantize_ref(hk.astype(np.float64))
+    assert np.array_equal(host(hq), kq)
+    assert np.array_equal(host(hs), ks)
+    n_mis, n_bad = explain_hq_mismatches(host(hq), host(hs), rq, rh)
+    say(f"  {name}: hq/hs mismatches vs oracle {n_mis} of {rq.size}, unexplained {n_bad}")
+    assert n_bad == 0 and n_mis <= 0.01 * rq.size
+    # cumulative group list gives the same bytes
+    hq0, hs0 = mx.gmm_swiglu_mxquant(u8_dev(aq), u8_dev(as_), u8_dev(wq), u8_dev(ws), i64_dev(np.cumsum(counts)), 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(hq0), host(hq)) and np.array_equal(host(hs0), host(hs))
+
+
+def test_gmm_swiglu_gate_up_closed_form():
+    """gate row outputs 2, up row outputs 3 -> h = silu(2) * 3 everywhere."""
+    K, I, E, M = 128, 64, 2, 40
+    say("gmm_swiglu_mxquant closed form")
+    aq = np.zeros((M, K), np.uint8); aq[:, 0] = 0x38
+    as_ = np.full((M, K // 64, 2), 127, np.uint8)
+    w = np.zeros((E, 2 * I, K), np.uint8)
+    w[:, :I, 0] = 0x40
+    w[:, I:, 0] = 0x44
+    ws = np.full((E, 2 * I, K // 64, 2), 127, np.uint8)
+    hq, hs, h = mx.gmm_swiglu_mxquant(u8_dev(aq), u8_dev(as_), u8_dev(w), u8_dev(ws), i64_dev([15, 25]), 1,
+                                      h_debug=True)
+    torch.cuda.synchronize()
+    expect = 2.0 / (1 + np.exp(-2.0)) * 3.0
+    assert np.allclose(host(h), expect, rtol=2e-6)
+    rq, rs, _ = moe_ref.gmm_swiglu_mxquant_ref(aq, as_, w, ws, np.array([15, 25]), 1, I)
+    assert np.array_equal(host(hq), rq) and np.array_equal(host(hs), rs)
+
+
+# --------------------------------------------------------------------------
+# finalize
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(64, 256, 2), (33, 2048, 8), (5, 4096, 1), (17, 128, 12)])
+def test_finalize_bitexact(shape):
+    T, K, k = shape
+    say(f"moe_finalize T={T} K={K} k={k}")
+    M = T * k
+    y = _rand_bf16((M, K), scale_spread=6)
+    w = RNG.random((T, k)).astype(np.float32)
+    eri = RNG.permutation(M).astype(np.int32)
+    out = mx.moe_finalize(bf16_dev(y), f32_dev(w), i32_dev(eri))
+    torch.cuda.synchronize()
+    ref = moe_ref.finalize_ref(y, w, eri)
+    assert np.array_equal(bf16_host(out), ref)
+
+
+def test_finalize_skips_invalid_rows():
+    T, K, k = 20, 64, 3
+    say("moe_finalize invalid rows")
+    M = T * k
+    y = _rand_bf16((M, K))
+    w = RNG.random((T, k)).astype(np.float32)
+    eri = RNG.permutation(M).astype(np.int32)
+    eri[[4, 9, 30]] = -1
+    eri[40] = M + 5
+    out = mx.moe_finalize(bf16_dev(y), f32_dev(w), i32_dev(eri))
+    torch.cuda.synchronize()
+    w2 = w.copy().reshape(-1)
+    bad = (eri < 0) | (eri >= M)
+    w2[bad] = 0.0
+    eri2 = np.where(bad, 0, eri)
+    ref = moe_ref.finalize_ref(y, w2.reshape(T, k), eri2)
+    assert np.array_equal(bf16_host(out), ref)
