@@ -56,9 +56,11 @@
  * it counts toward no expert, so sum(group_list) < T*k tells the caller), and
  * group lists are clamped to [0, M] rows.
  *
- * GPU shape limits (MX_ERR_UNSUPPORTED otherwise): GEMM reduction and output
- * dims (K, I, N, Kd of the GEMMs) multiples of 128; routing needs K % 32 == 0
- * and 1 <= k <= 256, E <= 1024; mx_quantize takes any Kd >= 1.
+ * GPU shape limits (MX_ERR_UNSUPPORTED otherwise): GEMM reduction dims (K of
+ * GEMM1, I of GEMM2) multiples of 128; GEMM2 output dim N a multiple of 256;
+ * GEMM1 intermediate size I a multiple of 128 (so the forward needs K % 256
+ * == 0 and I % 128 == 0); routing needs K % 32 == 0, 1 <= k <= 256 and
+ * E <= 1024; mx_quantize takes any Kd >= 1.
  */
 #ifndef MXMOE_H
 #define MXMOE_H

@@ -57,8 +57,8 @@ int check_forward_args(int64_t T, int64_t K, int64_t I, int64_t E, int64_t k) {
   int rc = check_route_args(T, K, k, E);
   if (rc) return rc;
   if (I <= 0) return fail(MX_ERR_INVALID_ARG, "moe_mxfp8_forward: bad I=%lld", (long long)I);
-  if (K % 128 != 0 || I % 128 != 0)
-    return fail(MX_ERR_UNSUPPORTED, "moe_mxfp8_forward: K=%lld and I=%lld must be multiples of 128",
+  if (K % 256 != 0 || I % 128 != 0)
+    return fail(MX_ERR_UNSUPPORTED, "moe_mxfp8_forward: K=%lld must be a multiple of 256 and I=%lld of 128",
                 (long long)K, (long long)I);
   return check_gmm_common("moe_mxfp8_forward", 1, T * k, K, E);
 }

@@ -17,19 +17,36 @@
 // register.  Output: lane l holds column l%32, rows 8q + 4*(l/32) + (0..3) in
 // accumulator elements 4q..4q+3.
 //
-// Tiling.  A workgroup of 4 waves computes a 128 (weight rows) x 128 (tokens)
-// tile; each wave a 64 x 64 quarter as 2 x 2 MFMA tiles.  K advances 128
-// bytes per step through an LDS double buffer (16 KB per operand per stage,
-// rows of 128 bytes with the 16-byte chunk index XOR-ed by row%8 so the 32
-// lanes reading one chunk column hit distinct banks).  Scales for the step
-// (4 bytes per row) are staged next to the tiles.
+// Tiling.  A workgroup of 8 waves (two per SIMD) computes a 256 (weight
+// rows) x 256 (tokens) tile; wave w computes a 128 x 64 part (rows
+// 128*(w%2), tokens 64*(w/2)) as 4 x 2 MFMA tiles, 128 fp32 accumulators per
+// lane.  Two waves per SIMD let one wave's LDS reads, DMA issue and epilogue
+// overlap the other's MFMAs.
 //
-// Scheduling.  The kernel is persistent: every workgroup derives the
-// per-expert row ranges and m-tile prefix from the device-resident group
-// list (no host synchronisation), then walks tiles t = blockIdx.x,
-// blockIdx.x + gridDim.x, ...; tile t is m-tile t / n_tiles (an m-tile never
-// straddles two experts) and n-tile t % n_tiles.  Skewed and empty experts
-// cost nothing beyond their own tiles.
+// Data movement.  K advances 128 bytes per stage through a two-slot LDS ring
+// (66 KB per slot: 256 rows x 128 B of each operand plus the u32 of 4 scale
+// bytes per row), filled by direct global->LDS loads (global_load_lds_dwordx4
+// / _dword, 1 KB per instruction, no staging registers).  Whole 128-byte rows
+// matter: measured on gfx950, 64-byte row pieces halve the L2->LDS rate.  The
+// loads are issued from inline assembly with explicit vmcnt accounting (the
+// compiler otherwise waits for every outstanding LDS DMA before any LDS
+// read) and are interleaved with the stage's MFMAs rather than issued in one
+// burst, so the memory pipeline is fed while the matrix cores run.  Each DMA
+// takes a uniform 64-bit base in scalar registers and a 32-bit per-lane
+// offset.  The 16-byte chunk index of a row is XOR-ed with (row/2)%8: the 16
+// lanes of one 256-byte LDS access (consecutive rows, one chunk column) then
+// hit 16 distinct 4-bank groups of the 64-bank LDS; the swizzle is applied on
+// the global side by choosing which chunk each DMA lane fetches.
+//
+// Scheduling.  The kernel is persistent (one workgroup per CU).  Every
+// workgroup derives the per-expert row ranges and m-tile prefix from the
+// device-resident group list (no host synchronisation).  Tile t is m-tile
+// t / n_tiles (an m-tile never straddles two experts) and n-tile t % n_tiles;
+// workgroup b takes tiles j*G + (b%8)*(G/8) + b/8, j = 0, 1, ..., so the
+// 32 CUs of one XCD (workgroups are dealt to XCDs round-robin) walk a
+// contiguous run of tiles: the n-tiles of an m-tile and the m-tiles of an
+// expert share that XCD's L2.  The stage stream runs across tile boundaries:
+// the next tile's first stage is fetched while the current tile finishes.
 #include <algorithm>
 
 #include "common.h"
@@ -38,14 +55,18 @@ namespace mxmoe {
 
 namespace {
 
-constexpr int BM = 128;  // token rows per tile
-constexpr int BN = 128;  // weight rows per tile
-constexpr int BK = 128;  // K bytes per step
-constexpr int kThreads = 256;
+constexpr int BM = 256;  // token rows per tile
+constexpr int BN = 256;  // weight rows per tile
+constexpr int BK = 128;  // K bytes per stage
+constexpr int kThreads = 512;
 constexpr int kMaxE = 1024;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 
 struct GmmParams {
   const uint8_t* a;    // [M, Kd] e4m3
@@ -66,22 +87,85 @@ struct GmmParams {
   float* hdbg;
 };
 
+constexpr int SK = 128;          // K bytes per stage (whole 128-byte rows)
+constexpr int kSlots = 2;        // LDS ring slots
+constexpr int kDmaPerStage = 9;  // per wave: 4 (A) + 4 (B) x 1 KB, 1 scale load
+
+struct Stage {
+  uint8_t a[BN * SK];
+  uint8_t b[BM * SK];
+  uint32_t sa[BN];
+  uint32_t sb[BM];
+};
+
 __device__ __forceinline__ int64_t group_count(const int64_t* gl, int type, int e) {
   if (type == 1) return gl[e];
   return gl[e] - (e > 0 ? gl[e - 1] : 0);
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+
+// 64 lanes x 16 B from global (uniform base + per-lane 32-bit offset) to LDS
+// [m0, m0 + 1024).
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+// 64 lanes x 4 B to LDS [m0, m0 + 256).
+__device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Workgroup barrier that first drains this wave's LDS reads, so no read of a
+// slot can still be pending when the next DMA into that slot is issued.
+__device__ __forceinline__ void barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// A value the whole wave agrees on, moved to scalar registers.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <class T>
+__device__ __forceinline__ const T* uniptr(const T* p) {
+  return reinterpret_cast<const T*>(uni64(reinterpret_cast<int64_t>(p)));
+}
+
+// Two floats -> two bf16 (round to nearest even) packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// silu(g) * u with the hardware exp and reciprocal (about 1 ulp each).
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+// Where one workgroup's tile lives.
+struct TileInfo {
+  int e, nt;
+  int64_t m0;
+  int rows_valid;
+};
+
+// Physical 16-byte chunk of logical chunk c in tile row r (128-byte rows).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
 template <bool kSwiglu>
 __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BN * BK];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BM * BK];
-  __shared__ uint32_t sSA[2][BN];
-  __shared__ uint32_t sSB[2][BM];
+  __shared__ __attribute__((aligned(16))) Stage st[kSlots];
   __shared__ int s_tile0[kMaxE + 1];
-  __shared__ int s_row0[kMaxE];
-  __shared__ int s_row1[kMaxE];
+  __shared__ int s_row0[kMaxE + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = p.E;
 
   // ---- per-expert row ranges and m-tile prefix (wave 0) -------------------
@@ -112,10 +196,8 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       const int64_t r0 = run < p.M ? run : p.M;
       const int64_t r1 = run + n[i] < p.M ? run + n[i] : p.M;
       tiles[i] = (int)((r1 - r0 + BM - 1) / BM);
-      if (e < E) {
-        s_row0[e] = (int)r0;
-        s_row1[e] = (int)r1;
-      }
+      if (e < E) s_row0[e] = (int)r0;
+      if (e == E - 1) s_row0[E] = (int)r1;
       tloc += tiles[i];
       run += n[i];
     }
@@ -140,179 +222,255 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   const int total = s_tile0[E] * n_tiles;
   const int64_t Kd = p.Kd;
   const int64_t srow = Kd / 32;  // scale bytes per row
-  const int nk = (int)(Kd / BK);
+  const int nk = (int)(Kd / SK); // stages per tile
+  const int G = gridDim.x;       // a multiple of 8 (host)
+  const int xcd_base = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  if (xcd_base >= total) return;
+  const int my_tiles = (total - xcd_base + G - 1) / G;
   const int wn = wave & 1, wm = wave >> 1;
   const int li = lane & 31, lg = lane >> 5;
+  // DMA lane mapping: an instruction fills 8 rows of 128 B; lane l lands at
+  // row l/8, physical chunk l%8, which holds logical chunk
+  // (l%8) ^ ((row/2)%8); for the 8-row groups at even and odd multiples of 8
+  // rows that is (l%8) ^ (l/16) and (l%8) ^ (l/16) ^ 4.
+  const int drow = lane >> 3;
+  const int dch_even = (lane & 7) ^ (lane >> 4);
+  const int dch_odd = dch_even ^ 4;
 
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int mt = tile / n_tiles, nt = tile - mt * n_tiles;
+  auto tile_info = [&](int t) __attribute__((always_inline)) -> TileInfo {
+    TileInfo ti;
+    const int mt = t / n_tiles;
+    ti.nt = t - mt * n_tiles;
     int lo = 0, hi = E - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_tile0[mid] <= mt) lo = mid; else hi = mid - 1;
     }
-    const int e = lo;
-    const int64_t m0 = s_row0[e] + (int64_t)(mt - s_tile0[e]) * BM;
-    const int64_t m_end = s_row1[e];
-    const int rows_valid = (int)std::min<int64_t>(BM, m_end - m0);
+    ti.e = uni(lo);
+    ti.m0 = uni64(s_row0[ti.e] + (int64_t)(mt - s_tile0[ti.e]) * BM);
+    ti.rows_valid = uni((int)std::min<int64_t>(BM, s_row0[ti.e + 1] - ti.m0));
+    return ti;
+  };
 
-    const uint8_t* we = p.w + (int64_t)e * p.Nw * Kd;
-    const uint8_t* wse = p.ws + (int64_t)e * p.Nw * srow;
-
-    // weight row (within the expert) held in tile row r
-    auto wrow = [&](int r) -> int64_t {
-      if (kSwiglu) {
-        const int64_t hc0 = (int64_t)nt * 64;
-        const int half = r >> 6, q = r & 63;
-        return q < 32 ? hc0 + 32 * half + q : p.I + hc0 + 32 * half + (q - 32);
-      }
-      return (int64_t)nt * BN + r;
-    };
-    auto arow = [&](int r) -> int64_t { return std::min<int64_t>(m0 + r, m_end - 1); };
-
-    // per-thread global sources and LDS destinations of the 4+4 chunks
-    const uint8_t* gA[4];
-    const uint8_t* gB[4];
-    int lds_off[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + kThreads * i;
-      const int r = q >> 3, c = q & 7;
-      gA[i] = we + wrow(r) * Kd + c * 16;
-      gB[i] = p.a + arow(r) * Kd + c * 16;
-      lds_off[i] = r * BK + ((c ^ (r & 7)) << 4);
+  // ---- DMA cursor over the stage sequence (tile j, k stage ks) -------------
+  // wave w fetches rows [32w, 32w+32) of both operands (4 x 8 rows each);
+  // waves 0-3 fetch weight scale rows [64w, 64w+64), waves 4-7 token scale
+  // rows [64(w-4), 64(w-4)+64).  The cursor never passes the last stage: the
+  // fetches issued during the last stage repeat it into the slot no wave
+  // reads any more, so every fetch is in bounds and the loop has no branch
+  // around its loads.
+  struct Src {
+    const uint8_t* wrow;   // weight row held in LDS row 32*wave (uniform)
+    const uint8_t* arow;   // token row m0 (uniform)
+    const uint8_t* srowp;  // scale row base this wave fetches (uniform)
+    int last;              // M - 1 - m0 >= 0: last readable token row, relative to m0
+  };
+  auto make_src = [&](int t) __attribute__((always_inline)) -> Src {
+    const TileInfo ti = tile_info(t);
+    Src s;
+    int64_t wbase, sbase;  // weight rows of this wave's data and scale slabs
+    if (kSwiglu) {
+      // LDS rows [128h, 128h+64) hold gate rows, [128h+64, 128h+128) up rows
+      // of h columns [hc0 + 64h, hc0 + 64h + 64), h = 0, 1
+      const int64_t hc0 = (int64_t)ti.nt * (BN / 2);
+      const int q = wave & 3;
+      wbase = (q < 2 ? 0 : p.I - 64) + hc0 + 64 * (wave >> 2) + 32 * q;
+      sbase = ((wave & 1) ? p.I : 0) + hc0 + 64 * ((wave & 3) >> 1);
+    } else {
+      wbase = (int64_t)ti.nt * BN + 32 * wave;
+      sbase = (int64_t)ti.nt * BN + 64 * (wave & 3);
     }
-    const uint8_t* gS = tid < BN ? wse + wrow(tid) * srow : p.as + arow(tid - BN) * srow;
+    const int64_t wr = (int64_t)ti.e * p.Nw;
+    s.wrow = uniptr(p.w + (wr + wbase) * Kd);
+    s.arow = uniptr(p.a + ti.m0 * Kd);
+    s.srowp = wave < 4 ? uniptr(p.ws + (wr + sbase) * srow) : uniptr(p.as + ti.m0 * srow);
+    s.last = uni((int)(p.M - 1 - ti.m0));
+    return s;
+  };
+  // per-lane parts of the DMA offsets
+  const uint32_t lane_off_even = (uint32_t)(drow * Kd + dch_even * 16);
+  const uint32_t lane_off_odd = (uint32_t)(drow * Kd + dch_odd * 16);
+  const uint32_t lane_s = (uint32_t)(lane * srow);
+  // scale fetch: waves 0-3 weight scales (64 rows from srowp), waves 4-7
+  // token scales (rows past M repeat the last row)
+  const uint32_t s_lds = wave < 4 ? (uint32_t)offsetof(Stage, sa) + (uint32_t)(256 * wave)
+                                  : (uint32_t)offsetof(Stage, sb) + (uint32_t)(256 * (wave - 4));
+  auto s_voff = [&](int last) __attribute__((always_inline)) -> uint32_t {
+    return wave < 4 ? lane_s : (uint32_t)(std::min(64 * (wave - 4) + lane, last) * srow);
+  };
+  int dks = 0;   // k stage the cursor points at
+  Src dsrc = make_src(xcd_base);
+  int dslot = 0;
+  const uint32_t st_base = lds_addr(&st[0]);
+  // one DMA instruction of the cursor's stage: i = 0..3 weight rows, 4..7
+  // token rows, 8 scales
+  auto dma_part = [&](int i) __attribute__((always_inline)) {
+    const uint32_t slot = st_base + (uint32_t)dslot * (uint32_t)sizeof(Stage);
+    const int ko = dks * SK;
+    if (i < 4) {
+      const uint8_t* src = dsrc.wrow + (int64_t)(8 * i) * Kd + ko;
+      dma16((i & 1) ? lane_off_odd : lane_off_even, src,
+            slot + (uint32_t)offsetof(Stage, a) + (uint32_t)((32 * wave + 8 * i) * SK));
+    } else if (i < 8) {
+      const int j = i - 4;
+      const int r = std::min(32 * wave + 8 * j + drow, dsrc.last);   // rows past M repeat the last row
+      const uint32_t voff = (uint32_t)(r * Kd) + (uint32_t)(((j & 1) ? dch_odd : dch_even) * 16);
+      dma16(voff, dsrc.arow + ko, slot + (uint32_t)offsetof(Stage, b) + (uint32_t)((32 * wave + 8 * j) * SK));
+    } else {
+      dma4(s_voff(dsrc.last), dsrc.srowp + dks * 4, slot + s_lds);
+    }
+  };
+  // Advance the cursor by one stage; `next` is the source of this
+  // workgroup's next tile, `has_next` whether there is one.  Selects only, so
+  // the stage loop stays one basic block.
+  auto dma_advance = [&](const Src& next, bool has_next) __attribute__((always_inline)) {
+    dslot ^= 1;
+    const bool inc = dks + 1 < nk;
+    const bool wrap = !inc && has_next;
+    dks = inc ? dks + 1 : (wrap ? 0 : dks);
+    dsrc.wrow = wrap ? next.wrow : dsrc.wrow;
+    dsrc.arow = wrap ? next.arow : dsrc.arow;
+    dsrc.srowp = wrap ? next.srowp : dsrc.srowp;
+    dsrc.last = wrap ? next.last : dsrc.last;
+  };
 
-    // Register-staged double buffer: step ks computes from LDS buffer ks&1
-    // while the loads of step ks+1 are in flight; the last step re-loads
-    // step nk-1 (in bounds, result unused) so the loop has no branches.
-    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-    uint32_t rs;
-#define MX_GMM_LOAD(ks_)                                                  \
-    do {                                                                  \
-      const int64_t o_ = (int64_t)(ks_) * BK;                             \
-      ra0 = *reinterpret_cast<const uint4*>(gA[0] + o_);                  \
-      ra1 = *reinterpret_cast<const uint4*>(gA[1] + o_);                  \
-      ra2 = *reinterpret_cast<const uint4*>(gA[2] + o_);                  \
-      ra3 = *reinterpret_cast<const uint4*>(gA[3] + o_);                  \
-      rb0 = *reinterpret_cast<const uint4*>(gB[0] + o_);                  \
-      rb1 = *reinterpret_cast<const uint4*>(gB[1] + o_);                  \
-      rb2 = *reinterpret_cast<const uint4*>(gB[2] + o_);                  \
-      rb3 = *reinterpret_cast<const uint4*>(gB[3] + o_);                  \
-      rs = *reinterpret_cast<const uint32_t*>(gS + (int64_t)(ks_) * 4);   \
-    } while (0)
-#define MX_GMM_STORE(buf_)                                                \
-    do {                                                                  \
-      *reinterpret_cast<uint4*>(&sA[buf_][lds_off[0]]) = ra0;             \
-      *reinterpret_cast<uint4*>(&sA[buf_][lds_off[1]]) = ra1;             \
-      *reinterpret_cast<uint4*>(&sA[buf_][lds_off[2]]) = ra2;             \
-      *reinterpret_cast<uint4*>(&sA[buf_][lds_off[3]]) = ra3;             \
-      *reinterpret_cast<uint4*>(&sB[buf_][lds_off[0]]) = rb0;             \
-      *reinterpret_cast<uint4*>(&sB[buf_][lds_off[1]]) = rb1;             \
-      *reinterpret_cast<uint4*>(&sB[buf_][lds_off[2]]) = rb2;             \
-      *reinterpret_cast<uint4*>(&sB[buf_][lds_off[3]]) = rb3;             \
-      if (tid < BN) sSA[buf_][tid] = rs; else sSB[buf_][tid - BN] = rs;   \
-    } while (0)
+  // ---- LDS read addresses: row (li) part and the swizzled chunk parts ------
+  // Fragment rows differ by multiples of 32, so (row/2)%8 = (li/2)%8 for all.
+  const int sw = (li >> 1) & 7;
+  const uint32_t rd_a = (uint32_t)offsetof(Stage, a) + (uint32_t)((128 * wn + li) * SK);
+  const uint32_t rd_b = (uint32_t)offsetof(Stage, b) + (uint32_t)((64 * wm + li) * SK);
+  const uint32_t rd_sa = (uint32_t)offsetof(Stage, sa) + (uint32_t)((128 * wn + li) * 4);
+  const uint32_t rd_sb = (uint32_t)offsetof(Stage, sb) + (uint32_t)((64 * wm + li) * 4);
+  uint32_t chk[4];   // byte offset of logical chunk 2c + lg within a row
+#pragma unroll
+  for (int c = 0; c < 4; ++c) chk[c] = (uint32_t)(((2 * c + lg) ^ sw) << 4);
 
-    v16f acc[2][2];
+  // ---- prologue: stage 0 in flight ------------------------------------------
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+  for (int i = 0; i < kDmaPerStage; ++i) dma_part(i);
+  {
+    const bool has_next = my_tiles > 1;
+    dma_advance(has_next ? make_src(G + xcd_base) : dsrc, has_next);
+  }
 
-    MX_GMM_LOAD(0);
-    MX_GMM_STORE(0);
-    __syncthreads();
+  // ---- main loop: tiles of this workgroup, 128-byte K stages within ------
+  int g = 0;   // global stage index
+  for (int cj = 0; cj < my_tiles; ++cj) {
+    const TileInfo cur = tile_info(cj * G + xcd_base);
+    // source of the tile after this one: the cursor enters it during this
+    // tile's last stage
+    const bool has_next = cj + 1 < my_tiles;
+    const Src next = has_next ? make_src((cj + 1) * G + xcd_base) : dsrc;
+    v16f acc[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
+
     for (int ks = 0; ks < nk; ++ks) {
-      const int buf = ks & 1;
-      MX_GMM_LOAD(ks + 1 < nk ? ks + 1 : ks);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt0();   // this wave's part of stage g has landed
+      barrier();       // every wave's part has; slot g-1 is no longer read
+      const lds_u8* S = (const lds_u8*)(uintptr_t)(st_base + (uint32_t)(g & 1) * (uint32_t)sizeof(Stage));
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int c0 = 4 * s + lg, c1 = 4 * s + 2 + lg;
-        v8i fa[2], fb[2];
-        int sa[2], sb[2];
+        // k sub-step s covers logical chunks {4s + lg, 4s + 2 + lg} of each row
+        const int sh = 8 * (2 * s + lg);
+        v8i fa[4], fb[2];
+        int sa[4], sb[2];
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int ra_ = 64 * wn + 32 * f + li;
-          const uint8_t* baseA = &sA[buf][ra_ * BK];
-          const uint4 a0 = *reinterpret_cast<const uint4*>(baseA + ((c0 ^ (ra_ & 7)) << 4));
-          const uint4 a1 = *reinterpret_cast<const uint4*>(baseA + ((c1 ^ (ra_ & 7)) << 4));
+        for (int f = 0; f < 4; ++f) {
+          const lds_u8* pa = S + rd_a + f * 32 * SK;
+          const u32x4 a0 = *reinterpret_cast<lds_u32x4*>(pa + chk[2 * s]);
+          const u32x4 a1 = *reinterpret_cast<lds_u32x4*>(pa + chk[2 * s + 1]);
           fa[f] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-          sa[f] = (int)(sSA[buf][ra_] >> (8 * (2 * s + lg)));
-          const int rb_ = 64 * wm + 32 * f + li;
-          const uint8_t* baseB = &sB[buf][rb_ * BK];
-          const uint4 b0 = *reinterpret_cast<const uint4*>(baseB + ((c0 ^ (rb_ & 7)) << 4));
-          const uint4 b1 = *reinterpret_cast<const uint4*>(baseB + ((c1 ^ (rb_ & 7)) << 4));
-          fb[f] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-          sb[f] = (int)(sSB[buf][rb_] >> (8 * (2 * s + lg)));
+          sa[f] = (int)(*reinterpret_cast<lds_u32*>(S + rd_sa + f * 128) >> sh);
         }
 #pragma unroll
-        for (int fn = 0; fn < 2; ++fn)
+        for (int f = 0; f < 2; ++f) {
+          const lds_u8* pb = S + rd_b + f * 32 * SK;
+          const u32x4 b0 = *reinterpret_cast<lds_u32x4*>(pb + chk[2 * s]);
+          const u32x4 b1 = *reinterpret_cast<lds_u32x4*>(pb + chk[2 * s + 1]);
+          fb[f] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+          sb[f] = (int)(*reinterpret_cast<lds_u32*>(S + rd_sb + f * 128) >> sh);
+        }
+        // 8 MFMAs, with one DMA instruction of the next stage after every
+        // second (the ninth at the very end)
 #pragma unroll
-          for (int fm = 0; fm < 2; ++fm)
-            acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fa[fn], fb[fm], acc[fn][fm], 0, 0, 0, sa[fn], 0, sb[fm]);
+        for (int m = 0; m < 8; ++m) {
+          const int fm = m >> 2, fn = m & 3;
+          acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[fn], fb[fm], acc[fn][fm], 0, 0, 0,
+                                                                         sa[fn], 0, sb[fm]);
+          if (m & 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            dma_part(4 * s + (m >> 1));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       }
-      MX_GMM_STORE(buf ^ 1);
-      __syncthreads();
+      dma_part(8);
+      dma_advance(next, has_next);
+      __builtin_amdgcn_sched_barrier(0);
+      ++g;
     }
-#undef MX_GMM_LOAD
-#undef MX_GMM_STORE
 
-    // ---- epilogue ----------------------------------------------------------
+    // ---- epilogue (the next tile's first stage is already in flight) --------
     if (!kSwiglu) {
       const int64_t N = p.Nw;
 #pragma unroll
       for (int fm = 0; fm < 2; ++fm) {
         const int mc = 64 * wm + 32 * fm + li;
-        if (mc >= rows_valid) continue;
-        uint16_t* yrow = p.y + (m0 + mc) * N + (int64_t)nt * BN + 64 * wn;
+        if (mc >= cur.rows_valid) continue;
+        uint16_t* yrow = p.y + (cur.m0 + mc) * N + (int64_t)cur.nt * BN + 128 * wn;
 #pragma unroll
-        for (int fn = 0; fn < 2; ++fn)
+        for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const v16f& c = acc[fn][fm];
             uint2 o;
-            o.x = f32_to_bf16(c[4 * q]) | (f32_to_bf16(c[4 * q + 1]) << 16);
-            o.y = f32_to_bf16(c[4 * q + 2]) | (f32_to_bf16(c[4 * q + 3]) << 16);
+            o.x = pack_bf16x2(c[4 * q], c[4 * q + 1]);
+            o.y = pack_bf16x2(c[4 * q + 2], c[4 * q + 3]);
             *reinterpret_cast<uint2*>(yrow + 32 * fn + 8 * q + 4 * lg) = o;
           }
       }
     } else {
       const int64_t I = p.I;
-      const int64_t hcol0 = (int64_t)nt * 64 + 32 * wn;   // first h column of this wave's block
 #pragma unroll
       for (int fm = 0; fm < 2; ++fm) {
         const int mc = 64 * wm + 32 * fm + li;
-        const bool ok = mc < rows_valid;
-        float h[16];
-        float amax = 0.0f;
+        const bool ok = mc < cur.rows_valid;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float g = acc[0][fm][v], u = acc[1][fm][v];
-          h[v] = g / (1.0f + __expf(-g)) * u;
-          amax = fmaxf(amax, fabsf(h[v]));
-        }
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const uint32_t sbyte = e8m0_from_amax(amax);
-        const float inv = e8m0_inverse(sbyte);
-        if (ok) {
-          const int64_t m = m0 + mc;
-          uint8_t* hrow = p.hq + m * I + hcol0;
+        for (int f = 0; f < 2; ++f) {
+          __builtin_amdgcn_sched_barrier(0);   // one 32x32 block at a time
+          // gate fragment f pairs with up fragment f + 2 (same h columns)
+          const int64_t hcol0 = (int64_t)cur.nt * (BN / 2) + 64 * wn + 32 * f;
+          float h[16];
+          float amax = 0.0f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<uint32_t*>(hrow + 8 * q + 4 * lg) =
-                e4m3x4(h[4 * q] * inv, h[4 * q + 1] * inv, h[4 * q + 2] * inv, h[4 * q + 3] * inv);
-          if (lg == 0) p.hs[m * (I / 32) + hcol0 / 32] = static_cast<uint8_t>(sbyte);
-          if (p.hdbg) {
-            float* drow = p.hdbg + m * I + hcol0;
+          for (int v = 0; v < 16; ++v) {
+            h[v] = swiglu(acc[f][fm][v], acc[f + 2][fm][v]);
+            amax = fmaxf(amax, fabsf(h[v]));
+          }
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          const uint32_t sbyte = e8m0_from_amax(amax);
+          const float inv = e8m0_inverse(sbyte);
+          if (ok) {
+            const int64_t m = cur.m0 + mc;
+            uint8_t* hrow = p.hq + m * I + hcol0;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              *reinterpret_cast<float4*>(drow + 8 * q + 4 * lg) =
-                  make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+              *reinterpret_cast<uint32_t*>(hrow + 8 * q + 4 * lg) =
+                  e4m3x4(h[4 * q] * inv, h[4 * q + 1] * inv, h[4 * q + 2] * inv, h[4 * q + 3] * inv);
+            if (lg == 0) p.hs[m * (I / 32) + hcol0 / 32] = static_cast<uint8_t>(sbyte);
+            if (p.hdbg) {
+              float* drow_ = p.hdbg + m * I + hcol0;
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4*>(drow_ + 8 * q + 4 * lg) =
+                    make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+            }
           }
         }
       }
@@ -320,20 +478,14 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   }
 }
 
-int g_occ[2] = {0, 0};
-
 template <bool kSwiglu>
 int launch(const GmmParams& p, hipStream_t stream, const char* name) {
   if (p.M == 0) return MX_OK;
-  int& occ = g_occ[kSwiglu ? 1 : 0];
-  if (occ == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gmm_kernel<kSwiglu>, kThreads, 0) != hipSuccess || n <= 0)
-      n = 1;
-    occ = n;
-  }
   const int64_t upper = ((p.M + BM - 1) / BM + p.E) * (int64_t)p.n_tiles;
-  const int64_t grid = std::min<int64_t>(upper, (int64_t)num_cus() * occ);
+  if (upper >= ((int64_t)1 << 31)) return fail(MX_ERR_UNSUPPORTED, "%s: too many tiles", name);
+  int64_t grid = (int64_t)num_cus() / 8 * 8;
+  if (grid < 8) grid = 8;
+  if (grid > (upper + 7) / 8 * 8) grid = (upper + 7) / 8 * 8;
   gmm_kernel<kSwiglu><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
   return check_launch(name);
 }
@@ -368,7 +520,7 @@ int launch_gmm_swiglu(const uint8_t* a, const uint8_t* as, const uint8_t* w13, c
                       uint8_t* hs, float* hdbg, hipStream_t stream) {
   GmmParams p{};
   p.a = a; p.as = as; p.w = w13; p.ws = w13s; p.group_list = gl; p.gl_type = gl_type;
-  p.E = (int)E; p.M = M; p.Kd = K; p.Nw = 2 * I; p.n_tiles = (int)(I / 64); p.I = I;
+  p.E = (int)E; p.M = M; p.Kd = K; p.Nw = 2 * I; p.n_tiles = (int)(I / (BN / 2)); p.I = I;
   p.hq = hq; p.hs = hs; p.hdbg = hdbg;
   return launch<true>(p, stream, "gmm_swiglu_mxquant");
 }
@@ -402,8 +554,8 @@ extern "C" int gmm_swiglu_mxquant(const void* a_u8, const void* a_s, const void*
   int rc = check_gmm_common("gmm_swiglu_mxquant", group_list_type, M, K, E);
   if (rc) return rc;
   if (I <= 0) return fail(MX_ERR_INVALID_ARG, "gmm_swiglu_mxquant: bad I=%lld", (long long)I);
-  if (I % 64 != 0)
-    return fail(MX_ERR_UNSUPPORTED, "gmm_swiglu_mxquant: I=%lld is not a multiple of 64", (long long)I);
+  if (I % (BN / 2) != 0)
+    return fail(MX_ERR_UNSUPPORTED, "gmm_swiglu_mxquant: I=%lld is not a multiple of %d", (long long)I, BN / 2);
   if (!group_list || (M > 0 && (!a_u8 || !a_s || !w13_u8 || !w13_s || !hq_u8 || !hs_u8)))
     return fail(MX_ERR_INVALID_ARG, "gmm_swiglu_mxquant: null pointer");
   if (reinterpret_cast<uintptr_t>(a_u8) % 16 || reinterpret_cast<uintptr_t>(w13_u8) % 16 ||

@@ -78,13 +78,13 @@ def test_route_validation(lib):
 
 def test_gmm_validation(lib):
     g = lib.gmm_mx
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, 128, 128, 4, FAKE, None) == INVALID   # bad type
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 100, 128, 4, FAKE, None) == UNSUPPORTED  # N % 128
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 96, 4, FAKE, None) == UNSUPPORTED   # Kd % 128
-    assert g(FAKE, FAKE, FAKE, FAKE, None, 1, 16, 128, 128, 4, FAKE, None) == INVALID     # null group list
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 128, 0, FAKE, None) == INVALID     # E = 0
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, 256, 128, 4, FAKE, None) == INVALID   # bad type
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 128, 4, FAKE, None) == UNSUPPORTED  # N % 256
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 256, 96, 4, FAKE, None) == UNSUPPORTED   # Kd % 128
+    assert g(FAKE, FAKE, FAKE, FAKE, None, 1, 16, 256, 128, 4, FAKE, None) == INVALID     # null group list
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 256, 128, 0, FAKE, None) == INVALID     # E = 0
     s = lib.gmm_swiglu_mxquant
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 96, 4, FAKE, FAKE, None, None) == UNSUPPORTED  # I % 64
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 64, 4, FAKE, FAKE, None, None) == UNSUPPORTED  # I % 128
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 16, 128, 128, 4, FAKE, FAKE, None, None) == INVALID
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 128, 4, None, FAKE, None, None) == INVALID
 
@@ -101,6 +101,7 @@ def test_forward_validation(lib):
     call = lambda T, K, I, E, k, ws=1 << 30: f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, K, I, E, k, FAKE, FAKE,
                                                ws, None)
     assert call(64, 256, 96, 8, 2) == UNSUPPORTED      # I % 128
+    assert call(64, 384, 128, 8, 2) == UNSUPPORTED     # K % 256
     assert call(64, 200, 128, 8, 2) == UNSUPPORTED     # K % 32
     assert call(64, 256, 128, 8, 9) == INVALID         # k > E
     assert call(64, 256, 128, 8, 2, ws=16) == WORKSPACE

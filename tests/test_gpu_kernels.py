@@ -203,10 +203,11 @@ def _mx_operands(M, Kd, E, N, spread=4):
 
 
 GMM_CASES = {
-    "ragged": ([0, 1, 127, 128, 129, 300, 0, 5], 256, 256),
-    "single-expert": ([515], 384, 128),
-    "tiny-rows": ([1, 1, 1, 2], 128, 384),
-    "wide-k": ([64, 200], 1024, 128),
+    "ragged": ([0, 1, 127, 128, 129, 255, 256, 257, 300, 0, 5], 256, 256),
+    "single-expert": ([515], 384, 256),
+    "tiny-rows": ([1, 1, 1, 2], 128, 512),
+    "wide-k": ([64, 200, 33], 1024, 256),
+    "multi-tile-n": ([700, 20], 256, 768),
 }
 
 
@@ -229,7 +230,7 @@ def test_gmm_mx_parity(name, gl_type):
 
 def test_gmm_mx_exact_cases():
     say("gmm_mx all-ones and single-nonzero")
-    M, K, N, E = 300, 256, 128, 3
+    M, K, N, E = 300, 256, 256, 3
     aq = np.full((M, K), 0x38, np.uint8)
     as_ = np.full((M, K // 64, 2), 127, np.uint8)
     wq = np.full((E, N, K), 0x38, np.uint8)
@@ -249,9 +250,32 @@ def test_gmm_mx_exact_cases():
     assert np.array_equal(mx_ref.bf16_to_f64(bf16_host(y)), ref)
 
 
+def test_gmm_mx_bf16_rounding_is_rne():
+    """Exact fp32 sums that need rounding to bf16 (including exact ties) must
+    round to nearest even, as the oracle does."""
+    say("gmm_mx bf16 rounding")
+    rng = np.random.default_rng(11)
+    M, K, N, E = 256, 128, 256, 1
+    aq = np.zeros((M, K), np.uint8)
+    # 256 + small terms: the sum needs more than bf16's 8 significant bits
+    aq[:, 0] = 0x78                                        # 256
+    small = np.array([0x38, 0x30, 0x28, 0x20, 0x3C, 0x34, 0x00], np.uint8)   # 1, .5, .25, .125, 1.5, .75, 0
+    for j in range(1, 4):
+        aq[:, j] = rng.choice(small, M)
+    as_ = np.full((M, K // 64, 2), 127, np.uint8)
+    wq = np.zeros((E, N, K), np.uint8)
+    wq[0, :, :4] = np.where(rng.random((N, 4)) < 0.5, 0x38, 0xB8)   # +-1
+    wq[0, :, 0] = 0x38
+    ws = np.full((E, N, K // 64, 2), 127, np.uint8)
+    y = mx.gmm_mx(u8_dev(aq), u8_dev(as_), u8_dev(wq), u8_dev(ws), i64_dev([M]), 1)
+    torch.cuda.synchronize()
+    ref = moe_ref.gmm_mx_ref(aq, as_, wq, ws, np.array([M]), 1)
+    assert np.array_equal(bf16_host(y), ref)
+
+
 def test_gmm_mx_guard_bands_and_untouched_rows():
     counts = np.array([0, 129, 0, 70], np.int64)
-    M, Kd, N, E = 250, 128, 128, 4                     # 51 rows owned by no expert
+    M, Kd, N, E = 250, 128, 256, 4                     # 51 rows owned by no expert
     say("gmm_mx guard bands")
     aq, as_, wq, ws = _mx_operands(M, Kd, E, N)
     raw, y = guard_alloc(M * N, torch.bfloat16, fill=0x5A)
@@ -263,9 +287,9 @@ def test_gmm_mx_guard_bands_and_untouched_rows():
 
 
 GMM1_CASES = {
-    "ragged": ([3, 0, 128, 129, 1, 260], 256, 128),
+    "ragged": ([3, 0, 128, 129, 1, 260, 256, 511], 256, 128),
     "wide-i": ([70, 150], 128, 384),
-    "single": ([1], 512, 64),
+    "single": ([1], 512, 128),
 }
 
 
@@ -299,7 +323,7 @@ def test_gmm_swiglu_mxquant_parity(name):
 
 def test_gmm_swiglu_gate_up_closed_form():
     """gate row outputs 2, up row outputs 3 -> h = silu(2) * 3 everywhere."""
-    K, I, E, M = 128, 64, 2, 40
+    K, I, E, M = 128, 128, 2, 40
     say("gmm_swiglu_mxquant closed form")
     aq = np.zeros((M, K), np.uint8); aq[:, 0] = 0x38
     as_ = np.full((M, K // 64, 2), 127, np.uint8)
