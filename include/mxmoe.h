@@ -61,6 +61,12 @@
  * GEMM1 intermediate size I a multiple of 128 (so the forward needs K % 256
  * == 0 and I % 128 == 0); routing needs K % 32 == 0, 1 <= k <= 256 and
  * E <= 1024; mx_quantize takes any Kd >= 1.
+ *
+ * Alignment (MX_ERR_UNSUPPORTED otherwise): e4m3 payload and bf16 tensors
+ * that the GEMMs, routing and finalize read or write (x, xq, a, w, w13, w2,
+ * hq, y, out, the forward workspace) start on 16-byte boundaries, their scale
+ * tensors (a_s, w_s, w13_s, w2_s, hs) on 4-byte boundaries, h_f32_debug on 16.
+ * mx_quantize accepts any alignment (a slower path handles the rest).
  */
 #ifndef MXMOE_H
 #define MXMOE_H

@@ -65,6 +65,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 
@@ -418,34 +419,65 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
 
     // ---- epilogue (the next tile's first stage is already in flight) --------
     if (!kSwiglu) {
+      // The bf16 tile goes out through LDS so that every store writes whole
+      // 128-byte lines: each wave stages its 32-token x 128-feature halves
+      // (8 KB each) in its own part of the ring slot the last stage was read
+      // from (free once every wave is past the barrier below), then reads
+      // them back row-contiguous.  Staging layout: token row r at r*256;
+      // 16-byte chunk c at physical chunk c ^ (r%16), and its two 8-byte
+      // halves swapped when r >= 16, so both the writes (lane = token) and
+      // the reads (16 lanes per row) are free of bank conflicts.
       const int64_t N = p.Nw;
+      barrier();
+      lds_u8* stg = (lds_u8*)(uintptr_t)(st_base + (uint32_t)((g - 1) & 1) * (uint32_t)sizeof(Stage) +
+                                         (uint32_t)(wave * 8192));
+      const int rr = lane >> 4, rc = lane & 15;   // read-back: row within a group of 4, chunk
 #pragma unroll
       for (int fm = 0; fm < 2; ++fm) {
-        const int mc = 64 * wm + 32 * fm + li;
-        if (mc >= cur.rows_valid) continue;
-        uint16_t* yrow = p.y + (cur.m0 + mc) * N + (int64_t)cur.nt * BN + 128 * wn;
 #pragma unroll
         for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const v16f& c = acc[fn][fm];
-            uint2 o;
-            o.x = pack_bf16x2(c[4 * q], c[4 * q + 1]);
-            o.y = pack_bf16x2(c[4 * q + 2], c[4 * q + 3]);
-            *reinterpret_cast<uint2*>(yrow + 32 * fn + 8 * q + 4 * lg) = o;
+            const u32x2 o = {pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3])};
+            const int chunk = (4 * fn + q) ^ (li & 15);
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+                stg + li * 256 + chunk * 16 + ((lg ^ (li >> 4)) << 3)) = o;
           }
+        asm volatile("" ::: "memory");   // a wave's LDS accesses execute in issue order
+        u32x4 v[8];
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int r = 4 * it + rr;
+          v[it] = *reinterpret_cast<lds_u32x4*>(stg + r * 256 + ((rc ^ (r & 15)) << 4));
+          if (it >= 4) v[it] = u32x4{v[it].z, v[it].w, v[it].x, v[it].y};   // rows 16-31
+        }
+        const int mc0 = 64 * wm + 32 * fm + rr;
+        uint16_t* y0 = p.y + (cur.m0 + mc0) * N + (int64_t)cur.nt * BN + 128 * wn + 8 * rc;
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+          if (mc0 + 4 * it < cur.rows_valid) *reinterpret_cast<u32x4*>(y0 + 4 * it * N) = v[it];
+        asm volatile("" ::: "memory");   // a wave's LDS accesses execute in issue order
       }
     } else {
+      // SwiGLU, MX requant, and the stores through LDS: the two waves that
+      // share a 64-token block (wn = 0, 1: 64 h columns each) stage their
+      // e4m3 bytes into one 64 x 128-byte region (16-byte chunk index
+      // XOR-ed with (row/2)%8) and their scale bytes into 64 x 4 bytes, so
+      // after a barrier every row of the tile leaves as one full 128-byte
+      // line and one 4-byte scale word.
       const int64_t I = p.I;
+      barrier();
+      lds_u8* grp = (lds_u8*)(uintptr_t)(st_base + (uint32_t)((g - 1) & 1) * (uint32_t)sizeof(Stage) +
+                                         (uint32_t)(wm * (64 * 128 + 64 * 4)));
+      lds_u8* grp_s = grp + 64 * 128;
 #pragma unroll
       for (int fm = 0; fm < 2; ++fm) {
-        const int mc = 64 * wm + 32 * fm + li;
-        const bool ok = mc < cur.rows_valid;
+        const int t = 32 * fm + li;   // token row within the 64-token block
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           __builtin_amdgcn_sched_barrier(0);   // one 32x32 block at a time
           // gate fragment f pairs with up fragment f + 2 (same h columns)
-          const int64_t hcol0 = (int64_t)cur.nt * (BN / 2) + 64 * wn + 32 * f;
           float h[16];
           float amax = 0.0f;
 #pragma unroll
@@ -456,26 +488,45 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
           amax = fmaxf(amax, __shfl_xor(amax, 32));
           const uint32_t sbyte = e8m0_from_amax(amax);
           const float inv = e8m0_inverse(sbyte);
-          if (ok) {
-            const int64_t m = cur.m0 + mc;
-            uint8_t* hrow = p.hq + m * I + hcol0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int hc = 64 * wn + 32 * f + 8 * q + 4 * lg;   // h column within the tile
+            const int phys = ((hc >> 4) ^ ((t >> 1) & 7)) << 4 | (hc & 15);
+            *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(grp + t * 128 + phys) =
+                e4m3x4(h[4 * q] * inv, h[4 * q + 1] * inv, h[4 * q + 2] * inv, h[4 * q + 3] * inv);
+          }
+          if (lg == 0) grp_s[t * 4 + 2 * wn + f] = static_cast<uint8_t>(sbyte);
+          if (p.hdbg && 64 * wm + t < cur.rows_valid) {
+            float* drow_ = p.hdbg + (cur.m0 + 64 * wm + t) * I + (int64_t)cur.nt * (BN / 2) + 64 * wn + 32 * f;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              *reinterpret_cast<uint32_t*>(hrow + 8 * q + 4 * lg) =
-                  e4m3x4(h[4 * q] * inv, h[4 * q + 1] * inv, h[4 * q + 2] * inv, h[4 * q + 3] * inv);
-            if (lg == 0) p.hs[m * (I / 32) + hcol0 / 32] = static_cast<uint8_t>(sbyte);
-            if (p.hdbg) {
-              float* drow_ = p.hdbg + m * I + hcol0;
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<float4*>(drow_ + 8 * q + 4 * lg) =
-                    make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
-            }
+              *reinterpret_cast<float4*>(drow_ + 8 * q + 4 * lg) =
+                  make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
           }
         }
       }
+      barrier();
+      // wave wn stores rows [32 wn, 32 wn + 32) of its group: 8 lanes per row
+      const int64_t hc0 = (int64_t)cur.nt * (BN / 2);
+      u32x4 v[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = 32 * wn + 8 * it + (lane >> 3);
+        v[it] = *reinterpret_cast<lds_u32x4*>(grp + r * 128 + ((((lane & 7) ^ ((r >> 1) & 7))) << 4));
+      }
+      const uint32_t sw_word = li < 32 ? *reinterpret_cast<lds_u32*>(grp_s + (32 * wn + li) * 4) : 0u;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = 32 * wn + 8 * it + (lane >> 3);
+        if (64 * wm + r < cur.rows_valid)
+          *reinterpret_cast<u32x4*>(p.hq + (cur.m0 + 64 * wm + r) * I + hc0 + 16 * (lane & 7)) = v[it];
+      }
+      if (lg == 0 && 64 * wm + 32 * wn + li < cur.rows_valid)
+        *reinterpret_cast<uint32_t*>(p.hs + (cur.m0 + 64 * wm + 32 * wn + li) * (I / 32) + hc0 / 32) = sw_word;
     }
   }
+  // the final repeat fetch must land before the workgroup's LDS is released
+  wait_vmcnt0();
 }
 
 template <bool kSwiglu>
@@ -539,7 +590,7 @@ extern "C" int gmm_mx(const void* a_u8, const void* a_s, const void* w_u8, const
     return fail(MX_ERR_INVALID_ARG, "gmm_mx: null pointer");
   if (reinterpret_cast<uintptr_t>(a_u8) % 16 || reinterpret_cast<uintptr_t>(w_u8) % 16 ||
       reinterpret_cast<uintptr_t>(a_s) % 4 || reinterpret_cast<uintptr_t>(w_s) % 4 ||
-      reinterpret_cast<uintptr_t>(y_bf16) % 8)
+      reinterpret_cast<uintptr_t>(y_bf16) % 16)
     return fail(MX_ERR_UNSUPPORTED, "gmm_mx: misaligned pointer");
   return launch_gmm_mx(static_cast<const uint8_t*>(a_u8), static_cast<const uint8_t*>(a_s),
                        static_cast<const uint8_t*>(w_u8), static_cast<const uint8_t*>(w_s), group_list,
@@ -560,7 +611,8 @@ extern "C" int gmm_swiglu_mxquant(const void* a_u8, const void* a_s, const void*
     return fail(MX_ERR_INVALID_ARG, "gmm_swiglu_mxquant: null pointer");
   if (reinterpret_cast<uintptr_t>(a_u8) % 16 || reinterpret_cast<uintptr_t>(w13_u8) % 16 ||
       reinterpret_cast<uintptr_t>(a_s) % 4 || reinterpret_cast<uintptr_t>(w13_s) % 4 ||
-      reinterpret_cast<uintptr_t>(hq_u8) % 4 || reinterpret_cast<uintptr_t>(h_f32_debug) % 16)
+      reinterpret_cast<uintptr_t>(hq_u8) % 16 || reinterpret_cast<uintptr_t>(hs_u8) % 4 ||
+      reinterpret_cast<uintptr_t>(h_f32_debug) % 16)
     return fail(MX_ERR_UNSUPPORTED, "gmm_swiglu_mxquant: misaligned pointer");
   return launch_gmm_swiglu(static_cast<const uint8_t*>(a_u8), static_cast<const uint8_t*>(a_s),
                            static_cast<const uint8_t*>(w13_u8), static_cast<const uint8_t*>(w13_s), group_list,
