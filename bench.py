@@ -35,10 +35,24 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8/MXFP8 MFMA
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
 CFG = CONFIGS["prefill"]
 
-# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of the GEMM1 kernel, per launch,
-# scaled by the copy-kernel calibration (see profiles/); None until measured
-# for the current kernel.
-GEMM1_TRAFFIC_BYTES = None
+# HBM bytes per GEMM1 launch from two rocprofv3 --pmc passes (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for
+# a 1 GiB device-to-device copy in the same run (--copy-calibration).  Valid
+# only for the kernel source they were taken on: the SHA-256 of csrc/gmm.hip
+# is checked at run time and the traffic is reported as null on a mismatch.
+GEMM1_TRAFFIC = {"gmm_sha256": "9e11314a34526296974691a96cac508ffb12dfa9f0c91873723fdc14d5e57262",
+                 "fetch_bytes": 1.01414e+09, "write_bytes": 1.04228e+08}
+
+
+def gemm1_traffic():
+    if not GEMM1_TRAFFIC:
+        return None
+    import hashlib
+    src = os.path.join(ROOT, "mxfp8_block_scaled_topk_amd", "csrc", "gmm.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != GEMM1_TRAFFIC["gmm_sha256"]:
+            return None
+    return round(GEMM1_TRAFFIC["fetch_bytes"] + GEMM1_TRAFFIC["write_bytes"])
 
 
 def algorithmic(cfg, counts):
@@ -80,6 +94,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="finish with a 1 GiB device-to-device copy, the known-size kernel that "
+                         "calibrates the FETCH_SIZE / WRITE_SIZE hardware counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (one GPU holds all experts); "
@@ -151,7 +168,7 @@ def main():
     achieved = g1["flops"] / dur[dom] / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
-                "traffic": GEMM1_TRAFFIC_BYTES}
+                "traffic": gemm1_traffic()}
 
     rec = {
         "metric": "MoE layer tokens/s @16K prefill; grouped-GEMM MXFP8 MFMA % of peak",
@@ -173,6 +190,15 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(d)
     print(json.dumps(rec), flush=True)
