@@ -48,6 +48,7 @@
 // expert share that XCD's L2.  The stage stream runs across tile boundaries:
 // the next tile's first stage is fetched while the current tile finishes.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -68,6 +69,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+// LDS reads the compiler must leave where they are written (between the MFMAs
+// they overlap): volatile, so no IR pass hoists them.
+typedef __attribute__((address_space(3))) const volatile u32x4 lds_u32x4_v;
+typedef __attribute__((address_space(3))) const volatile uint8_t lds_u8_v;
 
 struct GmmParams {
   const uint8_t* a;    // [M, Kd] e4m3
@@ -122,6 +127,13 @@ __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)
 // slot can still be pending when the next DMA into that slot is issued.
 __device__ __forceinline__ void barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// The same value, opaque to the optimiser: address arithmetic derived from it
+// is done where it is used instead of being hoisted out of the tile loop
+// (which would keep dozens of per-lane addresses live through the k loop).
+__device__ __forceinline__ int opaque(int v) {
+  asm("" : "+v"(v));
+  return v;
 }
 // A value the whole wave agrees on, moved to scalar registers.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -264,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     const uint8_t* wrow;   // weight row held in LDS row 32*wave (uniform)
     const uint8_t* arow;   // token row m0 (uniform)
     const uint8_t* srowp;  // scale row base this wave fetches (uniform)
-    int last;              // M - 1 - m0 >= 0: last readable token row, relative to m0
+    int last;              // min(M - 1 - m0, BM - 1): last readable token row of the tile, relative to m0
   };
   auto make_src = [&](int t) __attribute__((always_inline)) -> Src {
     const TileInfo ti = tile_info(t);
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     s.wrow = uniptr(p.w + (wr + wbase) * Kd);
     s.arow = uniptr(p.a + ti.m0 * Kd);
     s.srowp = wave < 4 ? uniptr(p.ws + (wr + sbase) * srow) : uniptr(p.as + ti.m0 * srow);
-    s.last = uni((int)(p.M - 1 - ti.m0));
+    s.last = uni((int)std::min<int64_t>(p.M - 1 - ti.m0, BM - 1));
     return s;
   };
   // per-lane parts of the DMA offsets
@@ -293,46 +305,42 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   const uint32_t lane_off_odd = (uint32_t)(drow * Kd + dch_odd * 16);
   const uint32_t lane_s = (uint32_t)(lane * srow);
   // scale fetch: waves 0-3 weight scales (64 rows from srowp), waves 4-7
-  // token scales (rows past M repeat the last row)
+  // token scales (rows past M repeat the last row).  Offsets are byte
+  // offsets clamped with one min against a scalar cap, so the DMA path has
+  // no multiply and no branch.
   const uint32_t s_lds = wave < 4 ? (uint32_t)offsetof(Stage, sa) + (uint32_t)(256 * wave)
                                   : (uint32_t)offsetof(Stage, sb) + (uint32_t)(256 * (wave - 4));
+  const uint32_t s_lane = wave < 4 ? lane_s : (uint32_t)((64 * (wave - 4) + lane) * srow);
   auto s_voff = [&](int last) __attribute__((always_inline)) -> uint32_t {
-    return wave < 4 ? lane_s : (uint32_t)(std::min(64 * (wave - 4) + lane, last) * srow);
+    const uint32_t cap = wave < 4 ? 0xffffffffu : (uint32_t)(last * srow);
+    return std::min(s_lane, cap);
   };
-  int dks = 0;   // k stage the cursor points at
-  Src dsrc = make_src(xcd_base);
-  int dslot = 0;
+  // token rows of this wave's B part: row 32 wave + 8 j + drow, as a byte offset
+  const uint32_t b_row0 = (uint32_t)((32 * wave + drow) * Kd);
   const uint32_t st_base = lds_addr(&st[0]);
-  // one DMA instruction of the cursor's stage: i = 0..3 weight rows, 4..7
-  // token rows, 8 scales
-  auto dma_part = [&](int i) __attribute__((always_inline)) {
-    const uint32_t slot = st_base + (uint32_t)dslot * (uint32_t)sizeof(Stage);
-    const int ko = dks * SK;
+  // One DMA instruction of k stage ks of the tile whose source is `src`,
+  // into ring slot `slot`: i = 0..3 weight rows, 4..7 token rows, 8 scales.
+  auto dma_part = [&](int i, const Src& src, int ks, int slot) __attribute__((always_inline)) {
+    const uint32_t base = st_base + (uint32_t)slot * (uint32_t)sizeof(Stage);
+    const uint32_t ko = (uint32_t)(ks * SK);
+    // the row and k offsets go into the per-lane 32-bit offset, so the only
+    // scalar operand is the row base
     if (i < 4) {
-      const uint8_t* src = dsrc.wrow + (int64_t)(8 * i) * Kd + ko;
-      dma16((i & 1) ? lane_off_odd : lane_off_even, src,
-            slot + (uint32_t)offsetof(Stage, a) + (uint32_t)((32 * wave + 8 * i) * SK));
+      dma16(((i & 1) ? lane_off_odd : lane_off_even) + (uint32_t)(8 * i * Kd) + ko, src.wrow,
+            base + (uint32_t)offsetof(Stage, a) + (uint32_t)((32 * wave + 8 * i) * SK));
     } else if (i < 8) {
       const int j = i - 4;
-      const int r = std::min(32 * wave + 8 * j + drow, dsrc.last);   // rows past M repeat the last row
-      const uint32_t voff = (uint32_t)(r * Kd) + (uint32_t)(((j & 1) ? dch_odd : dch_even) * 16);
-      dma16(voff, dsrc.arow + ko, slot + (uint32_t)offsetof(Stage, b) + (uint32_t)((32 * wave + 8 * j) * SK));
+      // rows past M repeat the last row
+      const uint32_t row = std::min(b_row0 + (uint32_t)(8 * j * Kd), (uint32_t)(src.last * Kd));
+      const uint32_t voff = row + (uint32_t)(((j & 1) ? dch_odd : dch_even) * 16) + ko;
+      dma16(voff, src.arow, base + (uint32_t)offsetof(Stage, b) + (uint32_t)((32 * wave + 8 * j) * SK));
     } else {
-      dma4(s_voff(dsrc.last), dsrc.srowp + dks * 4, slot + s_lds);
+      dma4(s_voff(src.last) + (uint32_t)(ks * 4), src.srowp, base + s_lds);
     }
   };
-  // Advance the cursor by one stage; `next` is the source of this
-  // workgroup's next tile, `has_next` whether there is one.  Selects only, so
-  // the stage loop stays one basic block.
-  auto dma_advance = [&](const Src& next, bool has_next) __attribute__((always_inline)) {
-    dslot ^= 1;
-    const bool inc = dks + 1 < nk;
-    const bool wrap = !inc && has_next;
-    dks = inc ? dks + 1 : (wrap ? 0 : dks);
-    dsrc.wrow = wrap ? next.wrow : dsrc.wrow;
-    dsrc.arow = wrap ? next.arow : dsrc.arow;
-    dsrc.srowp = wrap ? next.srowp : dsrc.srowp;
-    dsrc.last = wrap ? next.last : dsrc.last;
+  auto dma_stage = [&](const Src& src, int ks, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kDmaPerStage; ++i) dma_part(i, src, ks, slot);
   };
 
   // ---- LDS read addresses: row (li) part and the swizzled chunk parts ------
@@ -345,93 +353,156 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   uint32_t chk[4];   // byte offset of logical chunk 2c + lg within a row
 #pragma unroll
   for (int c = 0; c < 4; ++c) chk[c] = (uint32_t)(((2 * c + lg) ^ sw) << 4);
+  // Fragments of one 64-wide k sub-step: A rows 128 wn + 32 f + li, B rows
+  // 64 wm + 32 f + li; sub-step s covers logical chunks {4s + lg, 4s + 2 + lg}
+  // of a row and scale byte 2s + lg of its stage word (read as one byte, so
+  // the value goes to the MFMA with no arithmetic between load and use).
+  auto slot_ptr = [&](int slot) __attribute__((always_inline)) {
+    uint32_t b = st_base + (uint32_t)slot * (uint32_t)sizeof(Stage);
+    asm("" : "+s"(b));   // opaque: one add per load instead of both slots' addresses kept live
+    return (const lds_u8*)(uintptr_t)b;
+  };
+  auto load_a = [&](int slot, int s, int f, v8i& frag, int& sc) __attribute__((always_inline)) {
+    const lds_u8* S = slot_ptr(slot);
+    const lds_u8* pa = S + rd_a + f * 32 * SK;
+    const u32x4 a0 = *reinterpret_cast<lds_u32x4_v*>(pa + chk[2 * s]);
+    const u32x4 a1 = *reinterpret_cast<lds_u32x4_v*>(pa + chk[2 * s + 1]);
+    frag = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    sc = (int)*reinterpret_cast<lds_u8_v*>(S + rd_sa + f * 128 + 2 * s + lg);
+  };
+  auto load_b = [&](int slot, int s, int f, v8i& frag, int& sc) __attribute__((always_inline)) {
+    const lds_u8* S = slot_ptr(slot);
+    const lds_u8* pb = S + rd_b + f * 32 * SK;
+    const u32x4 b0 = *reinterpret_cast<lds_u32x4_v*>(pb + chk[2 * s]);
+    const u32x4 b1 = *reinterpret_cast<lds_u32x4_v*>(pb + chk[2 * s + 1]);
+    frag = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    sc = (int)*reinterpret_cast<lds_u8_v*>(S + rd_sb + f * 128 + 2 * s + lg);
+  };
+  // ---- schedule ---------------------------------------------------------------
+  // Stage g (tile-local k stage ks) lives in slot g%2.  Sub-step 0 of stage g
+  // runs on fragments loaded during the previous sub-step and reloads them
+  // for sub-step 1 from the same slot.  Then one barrier: every wave is done
+  // reading slot g%2 and (after its own vmcnt wait) every part of stage g+1
+  // has landed in the other slot.  Sub-step 1 reloads the fragments of stage
+  // g+1's sub-step 0 and, after its first two MFMAs, issues the DMA of stage
+  // g+2 into slot g%2, a full stage ahead of its use.  A tile's last stage
+  // issues no DMA: its slot holds the epilogue's staging, and the DMA that
+  // was skipped follows the epilogue.
 
-  // ---- prologue: stage 0 in flight ------------------------------------------
-#pragma unroll
-  for (int i = 0; i < kDmaPerStage; ++i) dma_part(i);
-  {
-    const bool has_next = my_tiles > 1;
-    dma_advance(has_next ? make_src(G + xcd_base) : dsrc, has_next);
+  // prologue: stages 0 and 1 in flight
+  const Src first = make_src(xcd_base);
+  if (nk > 1) {
+    dma_stage(first, 0, 0);
+    dma_stage(first, 1, 1);
+  } else {
+    dma_stage(first, 0, 0);
+    if (my_tiles > 1) dma_stage(make_src(G + xcd_base), 0, 1);
   }
+  wait_vmcnt0();
+  barrier();
 
-  // ---- main loop: tiles of this workgroup, 128-byte K stages within ------
   int g = 0;   // global stage index
   for (int cj = 0; cj < my_tiles; ++cj) {
     const TileInfo cur = tile_info(cj * G + xcd_base);
-    // source of the tile after this one: the cursor enters it during this
-    // tile's last stage
+    const Src csrc = make_src(cj * G + xcd_base);
     const bool has_next = cj + 1 < my_tiles;
-    const Src next = has_next ? make_src((cj + 1) * G + xcd_base) : dsrc;
+    const Src nsrc = has_next ? make_src((cj + 1) * G + xcd_base) : csrc;
+    v8i fa[4], fb[2];
+    int sa[4], sb[2];
     v16f acc[4][2];
+    // The 8 MFMAs of one sub-step, B fragment 0 with A fragments 0..3, then B
+    // fragment 1 with A 0..3.  Each fragment is reloaded for the next sub-step
+    // (slot `nslot`, sub-step `ns`) right after its last MFMA, so the LDS reads
+    // overlap the matrix work; `extra(m)` runs after MFMA m (DMA issue).
+    auto substep = [&](int nslot, int ns, auto kReload, auto extra) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int fm = m >> 2, fn = m & 3;
+        acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[fn], fb[fm], acc[fn][fm], 0, 0, 0,
+                                                                       sa[fn], 0, sb[fm]);
+        // pin the MFMA here: without a use at this point the optimiser sinks
+        // the (side-effect free) MFMAs below the loads that were meant to
+        // overlap them, which also lengthens every fragment's live range
+        asm volatile("" : "+v"(acc[fn][fm]));
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(kReload)::value) {
+          if (m == 3) load_b(nslot, ns, 0, fb[0], sb[0]);
+          if (m >= 4) load_a(nslot, ns, m - 4, fa[m - 4], sa[m - 4]);
+          if (m == 7) load_b(nslot, ns, 1, fb[1], sb[1]);
+        }
+        extra(m);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto load_all = [&](int slot, int s) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int f = 0; f < 4; ++f) load_a(slot, s, f, fa[f], sa[f]);
+  #pragma unroll
+      for (int f = 0; f < 2; ++f) load_b(slot, s, f, fb[f], sb[f]);
+    };
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
+    // the tile's first fragments (stage g has landed: the prologue's barrier,
+    // or the middle barrier of the previous tile's last stage)
+    load_all(g & 1, 0);
 
-    for (int ks = 0; ks < nk; ++ks) {
+    // one k stage; kDma: issue stage g+2's DMA (every stage but the tile's last)
+    auto stage = [&](int ks, auto kDma) __attribute__((always_inline)) {
+      const int slot = g & 1;
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt0();   // this wave's part of stage g has landed
-      barrier();       // every wave's part has; slot g-1 is no longer read
-      const lds_u8* S = (const lds_u8*)(uintptr_t)(st_base + (uint32_t)(g & 1) * (uint32_t)sizeof(Stage));
+      substep(slot, 1, std::true_type{}, [&](int) {});
+      wait_vmcnt0();   // this wave's part of stage g+1 has landed
+      barrier();       // every wave's has, and nobody reads slot g%2 any more
+      if constexpr (decltype(kDma)::value) {
+        // DMA target: stage ks+2 of this tile, else stage 0 of the next tile,
+        // else (last tile) a repeat of this tile's last stage, never read
+        const bool in_tile = ks + 2 < nk;
+        Src t;
+        t.wrow = in_tile ? csrc.wrow : nsrc.wrow;
+        t.arow = in_tile ? csrc.arow : nsrc.arow;
+        t.srowp = in_tile ? csrc.srowp : nsrc.srowp;
+        t.last = in_tile ? csrc.last : nsrc.last;
+        const int tks = in_tile ? ks + 2 : (has_next ? 0 : nk - 1);
+        // the DMA goes out early in the sub-step (measured: issuing it over
+        // all eight MFMAs leaves the last loads too little time to land)
+        substep(slot ^ 1, 0, std::true_type{}, [&](int m) __attribute__((always_inline)) {
+          if (m == 0) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        // k sub-step s covers logical chunks {4s + lg, 4s + 2 + lg} of each row
-        const int sh = 8 * (2 * s + lg);
-        v8i fa[4], fb[2];
-        int sa[4], sb[2];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const lds_u8* pa = S + rd_a + f * 32 * SK;
-          const u32x4 a0 = *reinterpret_cast<lds_u32x4*>(pa + chk[2 * s]);
-          const u32x4 a1 = *reinterpret_cast<lds_u32x4*>(pa + chk[2 * s + 1]);
-          fa[f] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-          sa[f] = (int)(*reinterpret_cast<lds_u32*>(S + rd_sa + f * 128) >> sh);
-        }
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const lds_u8* pb = S + rd_b + f * 32 * SK;
-          const u32x4 b0 = *reinterpret_cast<lds_u32x4*>(pb + chk[2 * s]);
-          const u32x4 b1 = *reinterpret_cast<lds_u32x4*>(pb + chk[2 * s + 1]);
-          fb[f] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-          sb[f] = (int)(*reinterpret_cast<lds_u32*>(S + rd_sb + f * 128) >> sh);
-        }
-        // 8 MFMAs, with one DMA instruction of the next stage after every
-        // second (the ninth at the very end)
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int fm = m >> 2, fn = m & 3;
-          acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[fn], fb[fm], acc[fn][fm], 0, 0, 0,
-                                                                         sa[fn], 0, sb[fm]);
-          if (m & 1) {
-            __builtin_amdgcn_sched_barrier(0);
-            dma_part(4 * s + (m >> 1));
-            __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < 5; ++i) dma_part(i, t, tks, slot);
           }
-        }
+          if (m == 1) {
+#pragma unroll
+            for (int i = 5; i < kDmaPerStage; ++i) dma_part(i, t, tks, slot);
+          }
+        });
+      } else {
+        substep(slot ^ 1, 0, std::false_type{}, [&](int) {});   // the next tile reloads at its start
       }
-      dma_part(8);
-      dma_advance(next, has_next);
       __builtin_amdgcn_sched_barrier(0);
       ++g;
-    }
+    };
+    for (int ks = 0; ks + 1 < nk; ++ks) stage(ks, std::true_type{});
+    stage(nk - 1, std::false_type{});
 
-    // ---- epilogue (the next tile's first stage is already in flight) --------
+    // ---- epilogue (the next tile's first stage has landed) -------------------
     if (!kSwiglu) {
       // The bf16 tile goes out through LDS so that every store writes whole
       // 128-byte lines: each wave stages its 32-token x 128-feature halves
       // (8 KB each) in its own part of the ring slot the last stage was read
-      // from (free once every wave is past the barrier below), then reads
+      // from (no wave reads it and no DMA targets it any more), then reads
       // them back row-contiguous.  Staging layout: token row r at r*256;
       // 16-byte chunk c at physical chunk c ^ (r%16), and its two 8-byte
       // halves swapped when r >= 16, so both the writes (lane = token) and
       // the reads (16 lanes per row) are free of bank conflicts.
       const int64_t N = p.Nw;
-      barrier();
+      const int li = opaque(lane & 31), lg = opaque(lane >> 5), lane_e = opaque(lane);
       lds_u8* stg = (lds_u8*)(uintptr_t)(st_base + (uint32_t)((g - 1) & 1) * (uint32_t)sizeof(Stage) +
                                          (uint32_t)(wave * 8192));
-      const int rr = lane >> 4, rc = lane & 15;   // read-back: row within a group of 4, chunk
+      const int rr = lane_e >> 4, rc = lane_e & 15;   // read-back: row within a group of 4, chunk
 #pragma unroll
       for (int fm = 0; fm < 2; ++fm) {
 #pragma unroll
@@ -467,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       // after a barrier every row of the tile leaves as one full 128-byte
       // line and one 4-byte scale word.
       const int64_t I = p.I;
-      barrier();
+      const int li = opaque(lane & 31), lg = opaque(lane >> 5), lane_e = opaque(lane);
       lds_u8* grp = (lds_u8*)(uintptr_t)(st_base + (uint32_t)((g - 1) & 1) * (uint32_t)sizeof(Stage) +
                                          (uint32_t)(wm * (64 * 128 + 64 * 4)));
       lds_u8* grp_s = grp + 64 * 128;
@@ -511,21 +582,30 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       u32x4 v[4];
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const int r = 32 * wn + 8 * it + (lane >> 3);
-        v[it] = *reinterpret_cast<lds_u32x4*>(grp + r * 128 + ((((lane & 7) ^ ((r >> 1) & 7))) << 4));
+        const int r = 32 * wn + 8 * it + (lane_e >> 3);
+        v[it] = *reinterpret_cast<lds_u32x4*>(grp + r * 128 + ((((lane_e & 7) ^ ((r >> 1) & 7))) << 4));
       }
       const uint32_t sw_word = li < 32 ? *reinterpret_cast<lds_u32*>(grp_s + (32 * wn + li) * 4) : 0u;
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const int r = 32 * wn + 8 * it + (lane >> 3);
+        const int r = 32 * wn + 8 * it + (lane_e >> 3);
         if (64 * wm + r < cur.rows_valid)
-          *reinterpret_cast<u32x4*>(p.hq + (cur.m0 + 64 * wm + r) * I + hc0 + 16 * (lane & 7)) = v[it];
+          *reinterpret_cast<u32x4*>(p.hq + (cur.m0 + 64 * wm + r) * I + hc0 + 16 * (lane_e & 7)) = v[it];
       }
       if (lg == 0 && 64 * wm + 32 * wn + li < cur.rows_valid)
         *reinterpret_cast<uint32_t*>(p.hs + (cur.m0 + 64 * wm + 32 * wn + li) * (I / 32) + hc0 / 32) = sw_word;
     }
+    // every wave is done with the staging slot: issue the DMA the last stage
+    // skipped, global stage g + 1 (the next tile's stage 1, or with one stage
+    // per tile the stage 0 of the tile after next)
+    barrier();
+    if (nk > 1) {
+      if (has_next) dma_stage(nsrc, 1, (g + 1) & 1);
+    } else if (cj + 2 < my_tiles) {
+      dma_stage(make_src((cj + 2) * G + xcd_base), 0, (g + 1) & 1);
+    }
   }
-  // the final repeat fetch must land before the workgroup's LDS is released
+  // outstanding DMA must land before the workgroup's LDS is released
   wait_vmcnt0();
 }
 
