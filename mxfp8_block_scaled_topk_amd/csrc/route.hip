@@ -7,13 +7,18 @@
 //                        counts are order-free so atomics keep it exact)
 //   route_scan           one wave per expert: exclusive prefix of its counts
 //                        over the chunks, plus the expert's total (= group_list)
-//   route_scatter_quant  per chunk: the stable rank of every assignment among
-//                        the chunk's assignments to the same expert (wave
-//                        ballot match + per-wave counts in LDS), hence its row
-//                        p = offset[e] + prefix[e][chunk] + rank; writes both
-//                        maps; then MX-quantises each token of the chunk once,
-//                        in registers, and stores the payload and scales to
-//                        the token's k rows.
+//   route_scatter_quant  kSplit blocks per chunk: each finds the stable rank of
+//                        every assignment among the chunk's assignments to
+//                        the same expert (wave ballot match + per-wave counts
+//                        in LDS), hence its row p = offset[e] +
+//                        prefix[e][chunk] + rank; the first block writes both
+//                        maps; then each block MX-quantises its share of the
+//                        chunk's tokens once, in registers, and stores the
+//                        payload and scales to each token's k rows.  Several
+//                        blocks per chunk keep enough waves resident to hide
+//                        the load latency (one block per chunk left the
+//                        kernel at about 8 waves per CU at the 16K prefill
+//                        size).
 //
 // The order inside an expert is the flat index order, so the permutation is
 // deterministic and equals a stable sort by expert.
@@ -27,6 +32,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxE = 1024;
+constexpr int kSplit = 4;     // blocks per routing chunk in route_scatter_quant
 
 __global__ __launch_bounds__(kThreads) void route_hist(const int32_t* __restrict__ ids, int64_t M,
                                                        int k, int E, int tpc, int nchunks,
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter_quant(
   __shared__ int s_wsum[kThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = blockIdx.x;
+  const int c = blockIdx.x / kSplit, part = blockIdx.x % kSplit;
   for (int w = 0; w < kThreads / 64; ++w)
     for (int e = tid; e < E; e += kThreads) s_wcnt[w][e] = 0;
   block_exclusive_scan(totals, E, s_off, s_wsum);
@@ -142,21 +148,24 @@ __global__ __launch_bounds__(kThreads) void route_scatter_quant(
   if (valid) {
     for (int w = 0; w < wave; ++w) rank += s_wcnt[w][e];
     pos = s_off[e] + prefix[(int64_t)e * nchunks + c] + rank;
-    sorted_row[pos] = (int32_t)a;
+    if (part == 0) sorted_row[pos] = (int32_t)a;
   }
-  if (tid < na) eri[a] = pos;
+  if (part == 0 && tid < na) eri[a] = pos;
   s_pos[tid] = pos;
   __syncthreads();
 
   // ---- MX quant of the chunk's tokens, stored to each token's k rows ------
   const int64_t nb = K / 32;
   const int64_t s_stride = ((nb + 1) / 2) * 2;
+  // this block's tokens: [tb, te) of the chunk
   const int64_t t0 = (int64_t)c * tpc;
   const int ntok = (int)std::min<int64_t>((int64_t)tpc, T - t0);
-  const int64_t items = (int64_t)ntok * nb;
+  const int per = (tpc + kSplit - 1) / kSplit;
+  const int tb = std::min(part * per, ntok), te = std::min(tb + per, ntok);
+  const int64_t items = (int64_t)(te - tb) * nb;
   for (int64_t it = tid; it < items; it += kThreads) {
-    const int tl = (int)(it / nb);
-    const int64_t b = it - (int64_t)tl * nb;
+    const int tl = tb + (int)(it / nb);
+    const int64_t b = it - (int64_t)(tl - tb) * nb;
     const uint4* src = reinterpret_cast<const uint4*>(x + (t0 + tl) * K + b * 32);
     uint4 u[4];
 #pragma unroll
@@ -231,7 +240,7 @@ int launch_route_quant(const uint16_t* x, const int32_t* ids, int64_t T, int64_t
                                                                            group_list);
   rc = check_launch("route_scan");
   if (rc) return rc;
-  route_scatter_quant<<<dim3((unsigned)nch), dim3(kThreads), 0, stream>>>(
+  route_scatter_quant<<<dim3((unsigned)(nch * kSplit)), dim3(kThreads), 0, stream>>>(
       x, ids, T, K, (int)k, (int)E, nbits, (int)tpc, (int)nch, counts, totals, xq, xs, sorted_row, eri);
   return check_launch("route_scatter_quant");
 }
