@@ -13,12 +13,16 @@
 //                        in LDS), hence its row p = offset[e] +
 //                        prefix[e][chunk] + rank; the first block writes both
 //                        maps; then each block MX-quantises its share of the
-//                        chunk's tokens once, in registers, and stores the
-//                        payload and scales to each token's k rows.  Several
-//                        blocks per chunk keep enough waves resident to hide
-//                        the load latency (one block per chunk left the
-//                        kernel at about 8 waves per CU at the 16K prefill
-//                        size).
+//                        chunk's tokens once, in registers (two lanes per
+//                        32-element block, the block's amax combined with
+//                        one lane exchange), and stores the payload and
+//                        scales to each token's k rows: every store
+//                        instruction writes 1 KB of one row contiguously.
+//                        Several blocks per chunk keep enough waves resident
+//                        to hide the load latency (one block per chunk left
+//                        the kernel at about 8 waves per CU at the 16K
+//                        prefill size).  The kernel is bound by HBM writes
+//                        (k quantised copies of every token).
 //
 // The order inside an expert is the flat index order, so the permutation is
 // deterministic and equals a stable sort by expert.
@@ -32,7 +36,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxE = 1024;
-constexpr int kSplit = 4;     // blocks per routing chunk in route_scatter_quant
+constexpr int kSplit = 8;     // blocks per routing chunk in route_scatter_quant
 
 __global__ __launch_bounds__(kThreads) void route_hist(const int32_t* __restrict__ ids, int64_t M,
                                                        int k, int E, int tpc, int nchunks,
@@ -162,29 +166,37 @@ __global__ __launch_bounds__(kThreads) void route_scatter_quant(
   const int ntok = (int)std::min<int64_t>((int64_t)tpc, T - t0);
   const int per = (tpc + kSplit - 1) / kSplit;
   const int tb = std::min(part * per, ntok), te = std::min(tb + per, ntok);
-  const int64_t items = (int64_t)(te - tb) * nb;
+  const int64_t hpr = 2 * nb;   // half-blocks per token row
+  const int64_t items = (int64_t)(te - tb) * hpr;   // even, so lane pairs (2m, 2m+1) stay together
   for (int64_t it = tid; it < items; it += kThreads) {
-    const int tl = tb + (int)(it / nb);
-    const int64_t b = it - (int64_t)(tl - tb) * nb;
-    const uint4* src = reinterpret_cast<const uint4*>(x + (t0 + tl) * K + b * 32);
-    uint4 u[4];
+    const int tl = tb + (int)(it / hpr);
+    const int64_t hb = it - (int64_t)(tl - tb) * hpr;
+    const int64_t b = hb >> 1;
+    const int half = (int)(hb & 1);
+    const uint4* src = reinterpret_cast<const uint4*>(x + (t0 + tl) * K + b * 32 + half * 16);
+    const uint4 u0 = src[0], u1 = src[1];
+    float v[16];
+    unpack_bf16x8(u0, v);
+    unpack_bf16x8(u1, v + 8);
+    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) u[i] = src[i];
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) unpack_bf16x8(u[i], v + 8 * i);
-    uint32_t w[8];
-    const uint32_t sb = mx_block32(v, w);
-    const uint4 q0 = make_uint4(w[0], w[1], w[2], w[3]);
-    const uint4 q1 = make_uint4(w[4], w[5], w[6], w[7]);
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    const uint32_t sb = e8m0_from_amax(amax);
+    const float inv = e8m0_inverse(sb);
+    uint4 q;
+    q.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    q.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    q.z = e4m3x4(v[8] * inv, v[9] * inv, v[10] * inv, v[11] * inv);
+    q.w = e4m3x4(v[12] * inv, v[13] * inv, v[14] * inv, v[15] * inv);
     for (int j = 0; j < k; ++j) {
       const int p = s_pos[tl * k + j];
       if (p < 0) continue;
-      uint4* dst = reinterpret_cast<uint4*>(xq + (int64_t)p * K + b * 32);
-      dst[0] = q0;
-      dst[1] = q1;
-      xs[(int64_t)p * s_stride + b] = static_cast<uint8_t>(sb);
-      if ((nb & 1) && b == nb - 1) xs[(int64_t)p * s_stride + nb] = 0;
+      *reinterpret_cast<uint4*>(xq + (int64_t)p * K + b * 32 + half * 16) = q;
+      if (half == 0) {
+        xs[(int64_t)p * s_stride + b] = static_cast<uint8_t>(sb);
+        if ((nb & 1) && b == nb - 1) xs[(int64_t)p * s_stride + nb] = 0;
+      }
     }
   }
 }
