@@ -89,20 +89,45 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+# Argument checks.  The library receives raw pointers and sizes, so every
+# tensor is checked here for dtype, exact shape, contiguity and device before
+# the call: a tensor smaller than its sizes say would be read or written out
+# of bounds on the GPU.  Shape checks come first and residency on the GPU
+# last, so that shape errors are reported the same way on any device.
+
 def _need(t, dtype, name, ndim=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be on the GPU")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
 
 
-def _need_contig(t, name):
+def _need_shape(t, shape, name, dtype, device):
+    """t: a contiguous `dtype` tensor of exactly `shape` on `device`."""
+    _need(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _need_workspace(ws, nbytes, device, name="workspace"):
+    _need(ws, torch.uint8, name, 1)
+    if not ws.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ws.device != device:
+        raise ValueError(f"{name} must be on {device}, got {ws.device}")
+    if ws.numel() < nbytes:
+        raise ValueError(f"{name} has {ws.numel()} bytes, {nbytes} needed")
+
+
+def _need_gpu(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
 
 
 def _pairs(n):
@@ -123,9 +148,10 @@ def mx_quantize(x, q=None, s=None, stream=None):
         q = torch.empty(lead + (kd,), dtype=torch.uint8, device=x.device)
     if s is None:
         s = torch.empty(lead + (_pairs(kd), 2), dtype=torch.uint8, device=x.device)
-    _need(q, torch.uint8, "q"); _need(s, torch.uint8, "s")
-    _need_contig(q, "q"); _need_contig(s, "s")
+    _need_shape(q, lead + (kd,), "q", torch.uint8, x.device)
+    _need_shape(s, lead + (_pairs(kd), 2), "s", torch.uint8, x.device)
     ld = x2.stride(0) if rows > 1 else kd
+    _need_gpu(x, "x")
     rc = load().mx_quantize(_ptr(x2), rows, kd, ld, _ptr(q), _ptr(s), _stream(stream))
     _check(rc, "mx_quantize")
     return q, s
@@ -141,11 +167,12 @@ def moe_route_quant(x, topk_ids, E, out=None, workspace=None, stream=None):
     Returns (xq [M,K] u8, xs [M,K/64,2] u8, sorted_row [M] i32,
     expanded_row_idx [M] i32, group_list [E] i64 counts)."""
     _need(x, torch.bfloat16, "x", 2); _need(topk_ids, torch.int32, "topk_ids", 2)
-    _need_contig(x, "x"); _need_contig(topk_ids, "topk_ids")
     T, K = x.shape
     k = topk_ids.shape[1]
     M = T * k
     dev = x.device
+    _need_shape(x, (T, K), "x", torch.bfloat16, dev)
+    _need_shape(topk_ids, (T, k), "topk_ids", torch.int32, dev)
     if out is None:
         out = (torch.empty((M, K), dtype=torch.uint8, device=dev),
                torch.empty((M, _pairs(K), 2), dtype=torch.uint8, device=dev),
@@ -153,8 +180,16 @@ def moe_route_quant(x, topk_ids, E, out=None, workspace=None, stream=None):
                torch.empty(M, dtype=torch.int32, device=dev),
                torch.empty(E, dtype=torch.int64, device=dev))
     xq, xs, sr, eri, gl = out
+    _need_shape(xq, (M, K), "xq", torch.uint8, dev)
+    _need_shape(xs, (M, _pairs(K), 2), "xs", torch.uint8, dev)
+    _need_shape(sr, (M,), "sorted_row", torch.int32, dev)
+    _need_shape(eri, (M,), "expanded_row_idx", torch.int32, dev)
+    _need_shape(gl, (E,), "group_list", torch.int64, dev)
+    need = route_workspace_size(T, k, E)
     if workspace is None:
-        workspace = torch.empty(max(route_workspace_size(T, k, E), 256), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need_workspace(workspace, need, dev)
+    _need_gpu(x, "x")
     rc = load().moe_route_quant(_ptr(x), _ptr(topk_ids), T, K, k, E, _ptr(xq), _ptr(xs), _ptr(sr), _ptr(eri),
                                 _ptr(gl), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "moe_route_quant")
@@ -165,18 +200,25 @@ def gmm_swiglu_mxquant(a, a_s, w13, w13_s, group_list, group_list_type=GROUP_COU
                        h_debug=False, stream=None):
     """GEMM1 + SwiGLU + MX requant.  Returns (hq, hs) or (hq, hs, h) with h_debug."""
     _need(a, torch.uint8, "a", 2); _need(w13, torch.uint8, "w13", 3)
-    _need(group_list, torch.int64, "group_list", 1)
-    for t, n in [(a, "a"), (a_s, "a_s"), (w13, "w13"), (w13_s, "w13_s"), (group_list, "group_list")]:
-        _need_contig(t, n)
     M, K = a.shape
-    E, twoI, _ = w13.shape
+    E, twoI, Kw = w13.shape
+    if Kw != K or twoI % 2:
+        raise ValueError(f"w13 must be [E, 2I, {K}], got {tuple(w13.shape)}")
     I = twoI // 2
     dev = a.device
+    _need_shape(a, (M, K), "a", torch.uint8, dev)
+    _need_shape(a_s, (M, _pairs(K), 2), "a_s", torch.uint8, dev)
+    _need_shape(w13, (E, twoI, K), "w13", torch.uint8, dev)
+    _need_shape(w13_s, (E, twoI, _pairs(K), 2), "w13_s", torch.uint8, dev)
+    _need_shape(group_list, (E,), "group_list", torch.int64, dev)
     if out is None:
         out = (torch.empty((M, I), dtype=torch.uint8, device=dev),
                torch.empty((M, _pairs(I), 2), dtype=torch.uint8, device=dev))
     hq, hs = out
+    _need_shape(hq, (M, I), "hq", torch.uint8, dev)
+    _need_shape(hs, (M, _pairs(I), 2), "hs", torch.uint8, dev)
     h = torch.empty((M, I), dtype=torch.float32, device=dev) if h_debug else None
+    _need_gpu(a, "a")
     rc = load().gmm_swiglu_mxquant(_ptr(a), _ptr(a_s), _ptr(w13), _ptr(w13_s), _ptr(group_list),
                                    group_list_type, M, K, I, E, _ptr(hq), _ptr(hs), _ptr(h), _stream(stream))
     _check(rc, "gmm_swiglu_mxquant")
@@ -186,13 +228,20 @@ def gmm_swiglu_mxquant(a, a_s, w13, w13_s, group_list, group_list_type=GROUP_COU
 def gmm_mx(a, a_s, w, w_s, group_list, group_list_type=GROUP_COUNT, out=None, stream=None):
     """Grouped MX GEMM, bf16 output [M, N]."""
     _need(a, torch.uint8, "a", 2); _need(w, torch.uint8, "w", 3)
-    _need(group_list, torch.int64, "group_list", 1)
-    for t, n in [(a, "a"), (a_s, "a_s"), (w, "w"), (w_s, "w_s"), (group_list, "group_list")]:
-        _need_contig(t, n)
     M, Kd = a.shape
-    E, N, _ = w.shape
+    E, N, Kw = w.shape
+    if Kw != Kd:
+        raise ValueError(f"w must be [E, N, {Kd}], got {tuple(w.shape)}")
+    dev = a.device
+    _need_shape(a, (M, Kd), "a", torch.uint8, dev)
+    _need_shape(a_s, (M, _pairs(Kd), 2), "a_s", torch.uint8, dev)
+    _need_shape(w, (E, N, Kd), "w", torch.uint8, dev)
+    _need_shape(w_s, (E, N, _pairs(Kd), 2), "w_s", torch.uint8, dev)
+    _need_shape(group_list, (E,), "group_list", torch.int64, dev)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _need_shape(out, (M, N), "out", torch.bfloat16, dev)
+    _need_gpu(a, "a")
     rc = load().gmm_mx(_ptr(a), _ptr(a_s), _ptr(w), _ptr(w_s), _ptr(group_list), group_list_type, M, N, Kd, E,
                        _ptr(out), _stream(stream))
     _check(rc, "gmm_mx")
@@ -203,12 +252,18 @@ def moe_finalize(y, topk_w, expanded_row_idx, out=None, stream=None):
     """Weighted un-permute and sum: out [T, K] bf16."""
     _need(y, torch.bfloat16, "y", 2); _need(topk_w, torch.float32, "topk_w", 2)
     _need(expanded_row_idx, torch.int32, "expanded_row_idx")
-    for t, n in [(y, "y"), (topk_w, "topk_w"), (expanded_row_idx, "expanded_row_idx")]:
-        _need_contig(t, n)
     M, K = y.shape
     T, k = topk_w.shape
+    dev = y.device
+    _need_shape(y, (M, K), "y", torch.bfloat16, dev)
+    _need_shape(topk_w, (T, k), "topk_w", torch.float32, dev)
+    if expanded_row_idx.numel() != T * k:
+        raise ValueError(f"expanded_row_idx must hold T*k = {T * k} entries, got {expanded_row_idx.numel()}")
+    _need_shape(expanded_row_idx, tuple(expanded_row_idx.shape), "expanded_row_idx", torch.int32, dev)
     if out is None:
-        out = torch.empty((T, K), dtype=torch.bfloat16, device=y.device)
+        out = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+    _need_shape(out, (T, K), "out", torch.bfloat16, dev)
+    _need_gpu(y, "y")
     rc = load().moe_finalize(_ptr(y), _ptr(topk_w), _ptr(expanded_row_idx), T, K, k, M, _ptr(out),
                              _stream(stream))
     _check(rc, "moe_finalize")
@@ -228,18 +283,29 @@ def moe_mxfp8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, works
     w13 [E,2I,K] u8 + w13_s [E,2I,K/64,2], w2 [E,K,I] u8 + w2_s [E,K,I/64,2].
     Returns out [T,K] bf16."""
     _need(x, torch.bfloat16, "x", 2); _need(topk_ids, torch.int32, "topk_ids", 2)
-    _need(topk_w, torch.float32, "topk_w", 2); _need(w13, torch.uint8, "w13", 3); _need(w2, torch.uint8, "w2", 3)
-    for t, n in [(x, "x"), (topk_ids, "topk_ids"), (topk_w, "topk_w"), (w13, "w13"), (w13_s, "w13_s"),
-                 (w2, "w2"), (w2_s, "w2_s")]:
-        _need_contig(t, n)
+    _need(w13, torch.uint8, "w13", 3)
     T, K = x.shape
     k = topk_ids.shape[1]
-    E, twoI, _ = w13.shape
+    E, twoI, Kw = w13.shape
+    if Kw != K or twoI % 2:
+        raise ValueError(f"w13 must be [E, 2I, {K}], got {tuple(w13.shape)}")
     I = twoI // 2
+    dev = x.device
+    _need_shape(x, (T, K), "x", torch.bfloat16, dev)
+    _need_shape(topk_ids, (T, k), "topk_ids", torch.int32, dev)
+    _need_shape(topk_w, (T, k), "topk_w", torch.float32, dev)
+    _need_shape(w13, (E, twoI, K), "w13", torch.uint8, dev)
+    _need_shape(w13_s, (E, twoI, _pairs(K), 2), "w13_s", torch.uint8, dev)
+    _need_shape(w2, (E, K, I), "w2", torch.uint8, dev)
+    _need_shape(w2_s, (E, K, _pairs(I), 2), "w2_s", torch.uint8, dev)
     if out is None:
-        out = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
+        out = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+    _need_shape(out, (T, K), "out", torch.bfloat16, dev)
+    need = forward_workspace_size(T, K, I, E, k)
     if workspace is None:
-        workspace = forward_workspace(T, K, I, E, k, x.device)
+        workspace = forward_workspace(T, K, I, E, k, dev)
+    _need_workspace(workspace, need, dev)
+    _need_gpu(x, "x")
     rc = load().moe_mxfp8_forward(_ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w13), _ptr(w13_s), _ptr(w2),
                                   _ptr(w2_s), T, K, I, E, k, _ptr(out), _ptr(workspace), workspace.numel(),
                                   _stream(stream))

@@ -127,3 +127,89 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mx, "lib_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(mx.MxError):
         mx.load()
+
+
+# The binding checks every tensor's dtype, shape, contiguity and device before
+# it calls the library (the library sees only pointers and sizes), with shape
+# errors ahead of the GPU-residency check, so CPU tensors exercise them here.
+
+def _u8(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.uint8)
+
+
+def _gemm_args(M=16, K=128, N=256, E=4):
+    import torch
+    return dict(a=_u8(M, K), a_s=_u8(M, K // 64, 2), w=_u8(E, N, K), w_s=_u8(E, N, K // 64, 2),
+                gl=torch.zeros(E, dtype=torch.int64))
+
+
+def _raises(fn, pattern):
+    with pytest.raises((ValueError, TypeError), match=pattern):
+        fn()
+
+
+def test_binding_gmm_shape_checks(lib):
+    import torch
+    g = _gemm_args()
+    call = lambda **kw: mx.gmm_mx(*[kw.get(n, g[n]) for n in ("a", "a_s", "w", "w_s", "gl")],
+                                  out=kw.get("out"))
+    _raises(lambda: call(), "on the GPU")                                   # shapes fine, not on the GPU
+    _raises(lambda: call(a_s=_u8(16, 1, 2)), "a_s must have shape")        # wrong scale columns
+    _raises(lambda: call(a_s=_u8(8, 2, 2)), "a_s must have shape")         # wrong scale rows
+    _raises(lambda: call(w=_u8(4, 256, 64)), "w must be")                  # K of w != K of a
+    _raises(lambda: call(w_s=_u8(4, 128, 2, 2)), "w_s must have shape")
+    _raises(lambda: call(gl=torch.zeros(3, dtype=torch.int64)), "group_list must have shape")
+    _raises(lambda: call(gl=torch.zeros(4, dtype=torch.int32)), "group_list must be torch.int64")
+    _raises(lambda: call(out=torch.empty(16, 128, dtype=torch.bfloat16)), "out must have shape")
+    _raises(lambda: call(out=torch.empty(16, 256, dtype=torch.float32)), "out must be torch.bfloat16")
+    _raises(lambda: call(a=_u8(16, 256)[:, ::2]), "a must be contiguous")
+
+
+def test_binding_gmm_swiglu_shape_checks(lib):
+    import torch
+    g = _gemm_args(N=512)
+    call = lambda **kw: mx.gmm_swiglu_mxquant(*[kw.get(n, g[n]) for n in ("a", "a_s", "w", "w_s", "gl")],
+                                              out=kw.get("out"))
+    _raises(lambda: call(), "on the GPU")
+    _raises(lambda: call(w=_u8(4, 511, 128)), "w13 must be")               # odd 2I
+    _raises(lambda: call(w_s=_u8(4, 512, 1, 2)), "w13_s must have shape")
+    _raises(lambda: call(out=(_u8(16, 256), _u8(16, 4, 2))), "on the GPU")          # I = 256: correct
+    _raises(lambda: call(out=(_u8(16, 128), _u8(16, 4, 2))), "hq must have shape")
+    _raises(lambda: call(out=(_u8(16, 256), _u8(16, 3, 2))), "hs must have shape")
+    _raises(lambda: call(out=(_u8(16, 512)[:, ::2], _u8(16, 4, 2))), "hq must be contiguous")
+
+
+def test_binding_route_finalize_forward_shape_checks(lib):
+    import torch
+    T, K, k, E, I = 8, 256, 2, 4, 128
+    x = torch.zeros(T, K, dtype=torch.bfloat16)
+    ids = torch.zeros(T, k, dtype=torch.int32)
+    _raises(lambda: mx.moe_route_quant(x, ids, E), "on the GPU")
+    _raises(lambda: mx.moe_route_quant(x, ids, E, out=(_u8(T * k, K), _u8(T * k, 3, 2), ids.flatten(),
+                                                       ids.flatten(), torch.zeros(E, dtype=torch.int64))),
+            "xs must have shape")
+    _raises(lambda: mx.moe_route_quant(x, ids, E, workspace=_u8(1)), "workspace has 1 bytes")
+    y = torch.zeros(T * k, K, dtype=torch.bfloat16)
+    tw = torch.zeros(T, k, dtype=torch.float32)
+    _raises(lambda: mx.moe_finalize(y, tw, ids.flatten()), "on the GPU")
+    _raises(lambda: mx.moe_finalize(y, tw, ids.flatten()[:-1]), "expanded_row_idx must hold")
+    _raises(lambda: mx.moe_finalize(y, tw, ids.flatten(), out=torch.zeros(T, K // 2, dtype=torch.bfloat16)),
+            "out must have shape")
+    w13, w13_s = _u8(E, 2 * I, K), _u8(E, 2 * I, K // 64, 2)
+    w2, w2_s = _u8(E, K, I), _u8(E, K, I // 64, 2)
+    fwd = lambda **kw: mx.moe_mxfp8_forward(kw.get("x", x), kw.get("ids", ids), kw.get("tw", tw), w13, w13_s,
+                                            kw.get("w2", w2), kw.get("w2_s", w2_s), workspace=kw.get("ws"))
+    _raises(lambda: fwd(), "on the GPU")
+    _raises(lambda: fwd(tw=torch.zeros(T, k + 1)), "topk_w must have shape")
+    _raises(lambda: fwd(w2=_u8(E, K, 2 * I)), "w2 must have shape")
+    _raises(lambda: fwd(w2_s=_u8(E, K, 4, 2)), "w2_s must have shape")
+    _raises(lambda: fwd(ws=_u8(64)), "workspace has 64 bytes")
+
+
+def test_binding_mx_quantize_output_checks(lib):
+    import torch
+    x = torch.zeros(4, 100, dtype=torch.bfloat16)
+    _raises(lambda: mx.mx_quantize(x), "on the GPU")
+    _raises(lambda: mx.mx_quantize(x, s=_u8(4, 1, 2)), "s must have shape")   # ceil(100/64) = 2 pairs
+    _raises(lambda: mx.mx_quantize(x, q=_u8(4, 64)), "q must have shape")
