@@ -63,16 +63,29 @@ __global__ __launch_bounds__(kThreads) void route_scan(int32_t* __restrict__ cou
   if (e >= E) return;  // uniform per wave
   int32_t* row = counts + (int64_t)e * nchunks;
   int run = 0;
-  for (int base = 0; base < nchunks; base += 64) {
-    const int i = base + lane;
-    const int v = i < nchunks ? row[i] : 0;
-    int x = v;
+  // 512 chunks per round, 8 consecutive ones per lane: all loads of a round
+  // are in flight together (one memory round trip per 512 chunks)
+  for (int base = 0; base < nchunks; base += 512) {
+    const int i0 = base + 8 * lane;
+    int v[8];
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[j] = i0 + j < nchunks ? row[i0 + j] : 0;
+      s += v[j];
+    }
+    int x = s;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(x, off);
       if (lane >= off) x += y;
     }
-    if (i < nchunks) row[i] = run + x - v;
+    int excl = run + x - s;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (i0 + j < nchunks) row[i0 + j] = excl;
+      excl += v[j];
+    }
     run += __shfl(x, 63);
   }
   if (lane == 0) {
