@@ -25,7 +25,8 @@ define the method:
 Modules:
   mx_ref   -- e4m3 / e8m0 / bf16 codecs, MX block quantise / dequantise
   moe_ref  -- routing, grouped GEMMs, SwiGLU + requant, finalize, the whole
-              layer, and a per-token brute-force dense MoE
+              layer, a per-token brute-force dense MoE, and the top-k
+              softmax router upstream of the layer
 
 Every function states which passage it follows, or which reading of a silent
 passage it takes (the readings are listed in the design notes).

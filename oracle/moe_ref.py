@@ -23,6 +23,11 @@ Readings of what the pages leave open (numbered as in the design notes):
 * R18  finalize: out[t] = bf16(sum over j ascending of fp32(w[t,j] * y)),
        each multiply and add rounded to float32; no bias or residual.
 * R19  group_list is int64; type 0 = cumulative (inclusive), 1 = counts.
+* R28  the router (upstream of the layer): logits = x . Wg^T (+ a per-expert
+       bias) from the bf16 operands, softmax over the E experts, the k
+       experts with the largest logits in descending order (equal logits:
+       lower expert id first), weights = their softmax probabilities,
+       optionally renormalised to sum to 1.
 
 bf16 tensors are carried as uint16 bit patterns.
 """
@@ -301,3 +306,33 @@ def moe_unquantized_ref(x_bf16, topk_ids, topk_w, w13_bf16, w2_bf16):
             h = a[:I] / (1.0 + np.exp(-a[:I])) * a[I:]
             out[t] += float(topk_w[t, j]) * (w2[e] @ h)
     return out
+
+
+# --------------------------------------------------------------------------
+# router (upstream of the layer: produces the top-k ids and weights)
+# --------------------------------------------------------------------------
+
+def router_ref(x_bf16, gate_bf16, bias=None, k=8, renormalize=True):
+    """Top-k softmax router over a bf16 gate linear ("Quantization on Ascend",
+    MXFP8 for LLM MoE models, implementation notes: the router gate is a
+    plain linear layer kept in bf16 on the online path), reading R28.
+
+    Everything in float64: logits = x . Wg^T (+ bias), p = softmax(logits);
+    the k largest logits in descending order, equal logits taken lower id
+    first (a stable sort); weights p[ids], divided by their sum when
+    ``renormalize``.  Returns (ids int32 [T,k], weights float32 [T,k],
+    logits float64 [T,E]).
+    """
+    x = bf16_to_f64(np.asarray(x_bf16))
+    g = bf16_to_f64(np.asarray(gate_bf16))
+    logits = x @ g.T
+    if bias is not None:
+        logits = logits + np.asarray(bias, np.float64)[None, :]
+    ids = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    z = logits - logits.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=1, keepdims=True)
+    w = np.take_along_axis(p, ids, axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return ids.astype(np.int32), w.astype(np.float32), logits

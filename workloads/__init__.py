@@ -171,17 +171,24 @@ def _hot_cold_bias(cfg, base_logits, seed, target=0.20):
                       hot_token_frac=frac(bias[hot]))
 
 
+def router_inputs(cfg, x_bits, seed=0):
+    """The router's inputs: bf16 gate bits [E, K] N(0,0.02) and the per-expert
+    logit bias (float64 [E], None for plain routing), with an info dict."""
+    gate = normal_bf16(rng_for(seed, "gate"), (cfg.E, cfg.K), 0.02)
+    bias, info = None, {}
+    if cfg.routing in ("zipf", "hot_cold"):
+        logits = bf16_bits_to_f64(x_bits) @ bf16_bits_to_f64(gate).T
+        fn = _zipf_bias if cfg.routing == "zipf" else _hot_cold_bias
+        bias, info = fn(cfg, logits, seed)
+    return gate, bias, info
+
+
 def make_routing(cfg, x_bits, seed=0):
     """Router: bf16 gate [E, K] N(0,0.02); float64 logits; returns
     (topk_ids int32 [T,k], topk_w float32 [T,k], info dict)."""
-    gate = normal_bf16(rng_for(seed, "gate"), (cfg.E, cfg.K), 0.02)
+    gate, bias, info = router_inputs(cfg, x_bits, seed)
     logits = bf16_bits_to_f64(x_bits) @ bf16_bits_to_f64(gate).T
-    info = {}
-    if cfg.routing == "zipf":
-        bias, info = _zipf_bias(cfg, logits, seed)
-        logits = logits + bias[None, :]
-    elif cfg.routing == "hot_cold":
-        bias, info = _hot_cold_bias(cfg, logits, seed)
+    if bias is not None:
         logits = logits + bias[None, :]
     ids, w = _softmax_topk(logits, cfg.k)
     return ids, w, info
