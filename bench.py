@@ -13,7 +13,9 @@ finalize.
 Prints one JSON line.  After the headline loop a second loop runs the same
 four kernels through their own entry points with HIP events between them (on
 the stream they run on) to get each kernel's average duration; the roofline
-object is computed from those.
+object is computed from those.  The top-k router upstream of the layer
+(moe_router) is timed the same way and listed under "kernels" with
+"in_step": false: the layer takes the ids and weights as inputs.
 """
 
 import argparse
@@ -29,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import mxfp8_block_scaled_topk_amd as mx  # noqa: E402
-from workloads import CONFIGS, make_inputs  # noqa: E402
+from workloads import CONFIGS, make_inputs, router_inputs  # noqa: E402
 
 MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8/MXFP8 MFMA
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
@@ -162,6 +164,25 @@ def main():
             kd.update({"TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_FP8_PEAK_TFLOPS, 4),
                        "alg_flops": int(a["flops"])})
         kernels[n] = kd
+    # ---- the router upstream of the layer, timed on its own ----------------
+    gate_bits, bias, _ = router_inputs(cfg, d["x"])
+    gate = torch.from_numpy(gate_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    bias_d = None if bias is None else torch.from_numpy(bias.astype(np.float32)).to(dev)
+    r_out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev))
+    for _ in range(3):
+        mx.moe_router(x, gate, k, bias=bias_d, out=r_out)
+    rev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    rev[0].record(stream)
+    for _ in range(args.steps):
+        mx.moe_router(x, gate, k, bias=bias_d, out=r_out)
+    rev[1].record(stream)
+    torch.cuda.synchronize()
+    r_dur = rev[0].elapsed_time(rev[1]) * 1e-3 / args.steps
+    r_bytes = 2 * T * K + 2 * E * K + 8 * T * k      # x, gate, ids + weights
+    kernels["router"] = {"avg_us": round(r_dur * 1e6, 2), "hbm_GBs": round(r_bytes / r_dur / 1e9, 1),
+                         "hbm_frac": round(r_bytes / r_dur / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": int(r_bytes),
+                         "in_step": False}
+
     g1, g2 = alg["gemm1_swiglu_requant"], alg["gemm2"]
     gemm_tflops = (g1["flops"] + g2["flops"]) / (dur["gemm1_swiglu_requant"] + dur["gemm2"]) / 1e12
     dom = "gemm1_swiglu_requant"

@@ -12,6 +12,8 @@
  *   moe_finalize        weighted un-permute and sum of the top-k outputs
  *   moe_mxfp8_forward   the four steps above on one stream
  *   mx_quantize         stand-alone MX quantiser (weights at load time)
+ *   moe_router          top-k softmax router over a bf16 gate (upstream of
+ *                       the layer: produces the ids and weights it takes)
  *
  * Formats.  MXFP8 = e4m3 payload bytes plus one e8m0 scale byte (exponent +
  * 127, value 2^(byte-127)) per 32 consecutive elements along the reduction
@@ -186,6 +188,28 @@ int moe_mxfp8_forward(const void* x_bf16, const int32_t* topk_ids,
 int moe_mxfp8_forward_workspace_layout(int64_t T, int64_t K, int64_t I,
                                        int64_t E, int64_t k,
                                        size_t* offsets_host);
+
+/*
+ * Top-k softmax router over a bf16 gate linear, the step upstream of
+ * moe_route_quant ("Quantization on Ascend", MXFP8 for LLM MoE models,
+ * implementation notes: the router gate is a plain linear layer, kept in bf16
+ * on the online path).  For each token t:
+ *   logits[e] = sum_c x[t,c] * gate[e,c] (+ bias[e])   fp32 accumulation of
+ *               the exact bf16 products
+ *   topk_ids[t, :] = the k largest logits, descending (equal logits: the
+ *                    lower expert id first)
+ *   topk_w[t, j]   = softmax(logits)[topk_ids[t, j]], divided by the sum of
+ *                    the k selected when renormalize != 0
+ *   x bf16 [T, K], gate bf16 [E, K], bias fp32 [E] or NULL (-inf allowed:
+ *   that expert is never picked while a finite one is left);
+ *   topk_ids int32 [T, k], topk_w fp32 [T, k] (the inputs of moe_route_quant,
+ *   moe_finalize and moe_mxfp8_forward).
+ * Limits: K % 64 == 0, E <= 256 (MX_ERR_UNSUPPORTED); 1 <= k <= E
+ * (MX_ERR_INVALID_ARG); x and gate 16-byte aligned.
+ */
+int moe_router(const void* x_bf16, const void* gate_bf16, const float* bias,
+               int64_t T, int64_t K, int64_t E, int64_t k, int renormalize,
+               int32_t* topk_ids, float* topk_w, void* stream);
 
 /* Description of the last non-OK status returned on this thread. */
 const char* mx_last_error(void);

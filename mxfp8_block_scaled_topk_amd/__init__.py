@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "MxError", "lib_path", "load", "mx_quantize", "moe_route_quant", "gmm_swiglu_mxquant",
     "gmm_mx", "moe_finalize", "moe_mxfp8_forward", "forward_workspace", "forward_intermediates",
-    "route_workspace_size", "forward_workspace_size", "last_error",
+    "route_workspace_size", "forward_workspace_size", "last_error", "moe_router",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +61,7 @@ def load():
         "moe_mxfp8_forward_workspace_size": (SZ, [I64, I64, I64, I64, I64]),
         "moe_mxfp8_forward": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
         "moe_mxfp8_forward_workspace_layout": (I32, [I64, I64, I64, I64, I64, P]),
+        "moe_router": (I32, [P, P, P, I64, I64, I64, I64, I32, P, P, P]),
         "mx_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -334,3 +335,26 @@ def forward_intermediates(workspace, T, K, I, E, k):
         hs=view(6, M * _pairs(I) * 2, torch.uint8).view(M, _pairs(I), 2),
         y=view(7, M * K, torch.bfloat16).view(M, K),
     )
+
+
+def moe_router(x, gate, k, bias=None, renormalize=True, out=None, stream=None):
+    """Top-k softmax router: x [T,K] bf16, gate [E,K] bf16, optional bias [E]
+    fp32.  Returns (topk_ids [T,k] int32, topk_w [T,k] float32)."""
+    _need(x, torch.bfloat16, "x", 2); _need(gate, torch.bfloat16, "gate", 2)
+    T, K = x.shape
+    E = gate.shape[0]
+    dev = x.device
+    _need_shape(x, (T, K), "x", torch.bfloat16, dev)
+    _need_shape(gate, (E, K), "gate", torch.bfloat16, dev)
+    if bias is not None:
+        _need_shape(bias, (E,), "bias", torch.float32, dev)
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev))
+    ids, w = out
+    _need_shape(ids, (T, k), "topk_ids", torch.int32, dev)
+    _need_shape(w, (T, k), "topk_w", torch.float32, dev)
+    _need_gpu(x, "x")
+    rc = load().moe_router(_ptr(x), _ptr(gate), _ptr(bias), T, K, E, k, 1 if renormalize else 0, _ptr(ids), _ptr(w),
+                           _stream(stream))
+    _check(rc, "moe_router")
+    return ids, w

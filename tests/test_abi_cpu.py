@@ -213,3 +213,28 @@ def test_binding_mx_quantize_output_checks(lib):
     _raises(lambda: mx.mx_quantize(x), "on the GPU")
     _raises(lambda: mx.mx_quantize(x, s=_u8(4, 1, 2)), "s must have shape")   # ceil(100/64) = 2 pairs
     _raises(lambda: mx.mx_quantize(x, q=_u8(4, 64)), "q must have shape")
+
+
+def test_router_validation(lib):
+    f = lib.moe_router
+    call = lambda T, K, E, k: f(FAKE, FAKE, None, T, K, E, k, 1, FAKE, FAKE, None)
+    assert call(64, 128, 8, 9) == INVALID        # k > E
+    assert call(64, 128, 8, 0) == INVALID
+    assert call(-1, 128, 8, 2) == INVALID
+    assert call(64, 100, 8, 2) == UNSUPPORTED    # K % 64
+    assert call(64, 128, 300, 2) == UNSUPPORTED  # E > 256
+    assert f(None, FAKE, None, 64, 128, 8, 2, 1, FAKE, FAKE, None) == INVALID
+    assert f(ctypes.c_void_p(0x1008), FAKE, None, 64, 128, 8, 2, 1, FAKE, FAKE, None) == UNSUPPORTED
+    assert "aligned" in mx.last_error()
+
+
+def test_binding_router_shape_checks(lib):
+    import torch
+    x = torch.zeros(10, 128, dtype=torch.bfloat16)
+    g = torch.zeros(8, 128, dtype=torch.bfloat16)
+    _raises(lambda: mx.moe_router(x, g, 2), "on the GPU")
+    _raises(lambda: mx.moe_router(x, torch.zeros(8, 64, dtype=torch.bfloat16), 2), "gate must have shape")
+    _raises(lambda: mx.moe_router(x, g, 2, bias=torch.zeros(7)), "bias must have shape")
+    _raises(lambda: mx.moe_router(x, g, 2, bias=torch.zeros(8, dtype=torch.float64)), "bias must be torch.float32")
+    _raises(lambda: mx.moe_router(x, g, 2, out=(torch.zeros(10, 3, dtype=torch.int32), torch.zeros(10, 2))),
+            "topk_ids must have shape")
