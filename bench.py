@@ -15,7 +15,10 @@ four kernels through their own entry points with HIP events between them (on
 the stream they run on) to get each kernel's average duration; the roofline
 object is computed from those.  The top-k router upstream of the layer
 (moe_router) is timed the same way and listed under "kernels" with
-"in_step": false: the layer takes the ids and weights as inputs.
+"in_step": false: the layer takes the ids and weights as inputs.  So is a
+dense MXFP8 linear layer (mx_linear, T=16384, K=N=4096, offline-style
+pre-quantised weight): a second workload of the same MX GEMM, not part of
+the MoE step.
 """
 
 import argparse
@@ -31,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import mxfp8_block_scaled_topk_amd as mx  # noqa: E402
-from workloads import CONFIGS, make_inputs, router_inputs  # noqa: E402
+from workloads import CONFIGS, dense_linear_inputs, make_inputs, router_inputs  # noqa: E402
 
 MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8/MXFP8 MFMA
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
@@ -182,6 +185,30 @@ def main():
     kernels["router"] = {"avg_us": round(r_dur * 1e6, 2), "hbm_GBs": round(r_bytes / r_dur / 1e9, 1),
                          "hbm_frac": round(r_bytes / r_dur / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": int(r_bytes),
                          "in_step": False}
+
+    # ---- a dense MXFP8 linear layer, timed on its own ----------------------------
+    LT, LK, LN = 16384, 4096, 4096
+    lx, lwq, lws = dense_linear_inputs(LT, LK, LN)
+    lx = torch.from_numpy(lx.view(np.int16)).view(torch.bfloat16).to(dev)
+    lwq, lws = torch.from_numpy(lwq).to(dev), torch.from_numpy(lws).to(dev)
+    ly = torch.empty((LT, LN), dtype=torch.bfloat16, device=dev)
+    lws_buf = torch.empty(mx.linear_workspace_size(LT, LK), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        mx.mx_linear(lx, lwq, lws, out=ly, workspace=lws_buf)
+    rev[0].record(stream)
+    for _ in range(args.steps):
+        mx.mx_linear(lx, lwq, lws, out=ly, workspace=lws_buf)
+    rev[1].record(stream)
+    torch.cuda.synchronize()
+    l_dur = rev[0].elapsed_time(rev[1]) * 1e-3 / args.steps
+    l_flops = 2.0 * LT * LK * LN
+    l_bytes = 2 * LT * LK + LN * LK * (1 + 1 / 32) + 2 * LT * LN
+    kernels["dense_linear"] = {"avg_us": round(l_dur * 1e6, 2), "T": LT, "K": LK, "N": LN,
+                               "TFLOPs": round(l_flops / l_dur / 1e12, 1),
+                               "mfma_frac": round(l_flops / l_dur / 1e12 / MFMA_FP8_PEAK_TFLOPS, 4),
+                               "hbm_GBs": round(l_bytes / l_dur / 1e9, 1), "alg_bytes": int(l_bytes),
+                               "alg_flops": int(l_flops), "in_step": False}
+    del lx, lwq, lws, ly, lws_buf
 
     g1, g2 = alg["gemm1_swiglu_requant"], alg["gemm2"]
     gemm_tflops = (g1["flops"] + g2["flops"]) / (dur["gemm1_swiglu_requant"] + dur["gemm2"]) / 1e12

@@ -14,6 +14,7 @@
  *   mx_quantize         stand-alone MX quantiser (weights at load time)
  *   moe_router          top-k softmax router over a bf16 gate (upstream of
  *                       the layer: produces the ids and weights it takes)
+ *   mx_linear           dense MXFP8 linear layer (activation quant + MX GEMM)
  *
  * Formats.  MXFP8 = e4m3 payload bytes plus one e8m0 scale byte (exponent +
  * 127, value 2^(byte-127)) per 32 consecutive elements along the reduction
@@ -210,6 +211,25 @@ int moe_mxfp8_forward_workspace_layout(int64_t T, int64_t K, int64_t I,
 int moe_router(const void* x_bf16, const void* gate_bf16, const float* bias,
                int64_t T, int64_t K, int64_t E, int64_t k, int renormalize,
                int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Workspace bytes mx_linear needs for T tokens of K features. */
+size_t mx_linear_workspace_size(int64_t T, int64_t K);
+
+/*
+ * Dense MXFP8 linear layer ("Quantization on Ascend", MXFP8 (dense)
+ * implementation notes: weights MX-quantised once at load (see mx_quantize),
+ * activations MX-quantised per token at inference, block 32 along K, then the
+ * quantised matmul):
+ *   (xq, xs) = MX quantisation of x along K (as mx_quantize)
+ *   y[t, n]  = bf16_rne( sum over 32-blocks b of 2^(sx[t,b] + sw[n,b]) * (xq[t,b] . wq[n,b]) )
+ *   x bf16 [T, K]; w uint8 [N, K] e4m3; w_s uint8 [N, K/64, 2]; y bf16 [T, N].
+ * The workspace (mx_linear_workspace_size, 256-byte aligned) holds xq, xs
+ * and a one-entry group list.  Limits as gmm_mx with one group: K % 128 == 0,
+ * N % 256 == 0.
+ */
+int mx_linear(const void* x_bf16, const void* w_u8, const void* w_s,
+              int64_t T, int64_t K, int64_t N, void* y_bf16,
+              void* workspace, size_t ws_bytes, void* stream);
 
 /* Description of the last non-OK status returned on this thread. */
 const char* mx_last_error(void);

@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "MxError", "lib_path", "load", "mx_quantize", "moe_route_quant", "gmm_swiglu_mxquant",
     "gmm_mx", "moe_finalize", "moe_mxfp8_forward", "forward_workspace", "forward_intermediates",
-    "route_workspace_size", "forward_workspace_size", "last_error", "moe_router",
+    "route_workspace_size", "forward_workspace_size", "last_error", "moe_router", "mx_linear",
+    "linear_workspace_size",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +63,8 @@ def load():
         "moe_mxfp8_forward": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
         "moe_mxfp8_forward_workspace_layout": (I32, [I64, I64, I64, I64, I64, P]),
         "moe_router": (I32, [P, P, P, I64, I64, I64, I64, I32, P, P, P]),
+        "mx_linear_workspace_size": (SZ, [I64, I64]),
+        "mx_linear": (I32, [P, P, P, I64, I64, I64, P, P, SZ, P]),
         "mx_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -358,3 +361,33 @@ def moe_router(x, gate, k, bias=None, renormalize=True, out=None, stream=None):
                            _stream(stream))
     _check(rc, "moe_router")
     return ids, w
+
+
+def linear_workspace_size(T, K):
+    return int(load().mx_linear_workspace_size(T, K))
+
+
+def mx_linear(x, w, w_s, out=None, workspace=None, stream=None):
+    """Dense MXFP8 linear: x [T,K] bf16, w [N,K] e4m3 bytes, w_s [N,K/64,2]
+    e8m0 bytes (as mx_quantize makes them).  Returns y [T,N] bf16."""
+    _need(x, torch.bfloat16, "x", 2); _need(w, torch.uint8, "w", 2)
+    T, K = x.shape
+    N = w.shape[0]
+    dev = x.device
+    _need_shape(x, (T, K), "x", torch.bfloat16, dev)
+    _need_shape(w, (N, K), "w", torch.uint8, dev)
+    _need_shape(w_s, (N, _pairs(K), 2), "w_s", torch.uint8, dev)
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    _need_shape(out, (T, N), "out", torch.bfloat16, dev)
+    need = linear_workspace_size(T, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need_workspace(workspace, need, dev)
+    _need_gpu(x, "x")
+    if workspace.data_ptr() % 256:
+        raise ValueError("workspace must be 256-byte aligned")
+    rc = load().mx_linear(_ptr(x), _ptr(w), _ptr(w_s), T, K, N, _ptr(out), _ptr(workspace), workspace.numel(),
+                          _stream(stream))
+    _check(rc, "mx_linear")
+    return out

@@ -238,3 +238,26 @@ def test_binding_router_shape_checks(lib):
     _raises(lambda: mx.moe_router(x, g, 2, bias=torch.zeros(8, dtype=torch.float64)), "bias must be torch.float32")
     _raises(lambda: mx.moe_router(x, g, 2, out=(torch.zeros(10, 3, dtype=torch.int32), torch.zeros(10, 2))),
             "topk_ids must have shape")
+
+
+def test_linear_validation(lib):
+    f = lib.mx_linear
+    call = lambda T, K, N, ws=1 << 30: f(FAKE, FAKE, FAKE, T, K, N, FAKE, FAKE, ws, None)
+    assert call(64, 96, 256) == UNSUPPORTED      # K % 128
+    assert call(64, 128, 128) == UNSUPPORTED     # N % 256
+    assert call(64, 128, 0) == INVALID
+    assert call(-1, 128, 256) == INVALID
+    assert call(64, 128, 256, ws=16) == WORKSPACE
+    assert f(FAKE, None, FAKE, 64, 128, 256, FAKE, FAKE, 1 << 30, None) == INVALID
+    assert mx.linear_workspace_size(64, 128) >= 64 * 128 + 64 * 4 + 8
+    assert mx.linear_workspace_size(-1, 128) == 0
+
+
+def test_binding_linear_shape_checks(lib):
+    import torch
+    x = torch.zeros(10, 128, dtype=torch.bfloat16)
+    w, ws = _u8(256, 128), _u8(256, 2, 2)
+    _raises(lambda: mx.mx_linear(x, w, ws), "on the GPU")
+    _raises(lambda: mx.mx_linear(x, _u8(256, 64), ws), "w must have shape")
+    _raises(lambda: mx.mx_linear(x, w, _u8(256, 1, 2)), "w_s must have shape")
+    _raises(lambda: mx.mx_linear(x, w, ws, out=torch.zeros(10, 128, dtype=torch.bfloat16)), "out must have shape")

@@ -235,3 +235,12 @@ def make_inputs(cfg, seed=0, weights=True):
     if weights:
         d.update(make_weights(cfg, seed))
     return d
+
+
+def dense_linear_inputs(T, K, N, seed=0):
+    """A dense MXFP8 linear layer's inputs: x bf16 bits [T, K] N(0,1) and an
+    offline-style pre-quantised weight [N, K] (e4m3 bytes + pair-split e8m0
+    scale bytes, as ``_offline_checkpoint``)."""
+    x = normal_bf16(rng_for(seed, "x"), (T, K), 1.0, chunk_rows=4096)
+    wq, ws = _offline_checkpoint(rng_for(seed, "w2q"), rng_for(seed, "w2s"), (N, K))
+    return x, wq, ws
