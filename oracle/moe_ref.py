@@ -36,16 +36,29 @@ import numpy as np
 
 from .mx_ref import (
     BLOCK,
+    e2m1_decode,
     e4m3_decode,
     e8m0_decode,
     f32_to_bf16,
     bf16_to_f64,
+    fp4_unpack,
     mx_quantize_ref,
     scales_flat,
 )
 
 # e4m3 code -> value, without the block scale; NaN codes are never produced
 _E4M3_VALUES = e4m3_decode(np.arange(256))
+# e2m1 code -> value (codes 0..15)
+_E2M1_VALUES = e2m1_decode(np.arange(16))
+
+
+def weight_values(wq, w_format):
+    """Weight payload -> element values without the block scale: "e4m3"
+    bytes [..., Kd], or "e2m1" packed bytes [..., Kd/2] (W4A8, R29-R30)."""
+    if w_format == "e4m3":
+        return _E4M3_VALUES[np.asarray(wq)]
+    assert w_format == "e2m1", w_format
+    return _E2M1_VALUES[fp4_unpack(wq)]
 
 
 # --------------------------------------------------------------------------
@@ -135,23 +148,24 @@ def group_bounds(group_list, group_list_type, M):
 # grouped GEMMs
 # --------------------------------------------------------------------------
 
-def _mx_dot(aq, as_flat, wq, ws_flat):
+def _mx_dot(aq, as_flat, wq, ws_flat, w_format="e4m3"):
     """float32 result of the MX dot products of rows of A with rows of W (R16).
 
-    aq [n, Kd], wq [N, Kd] e4m3 codes; as_flat [n, nb], ws_flat [N, nb] scale
-    bytes, nb = Kd/32.  For each block b the e4m3 products are summed exactly:
-    every e4m3 value is an integer multiple of 2^-9 below 2^9, so products are
-    multiples of 2^-18 below 2^18 and a 32-term sum fits in 41 bits of a
-    float64 mantissa, whatever the order.  Block sums are scaled by
-    2^(sa + sb) (exact) and added in ascending block order in float64; the
-    total is rounded once to float32.  Returns float32 [n, N].
+    aq [n, Kd] e4m3 codes; wq [N, Kd] e4m3 codes, or [N, Kd/2] packed e2m1
+    (W4A8); as_flat [n, nb], ws_flat [N, nb] scale bytes, nb = Kd/32.  For
+    each block b the element products are summed exactly: every e4m3 value is
+    an integer multiple of 2^-9 below 2^9 (an e2m1 value a multiple of 2^-1 up
+    to 6), so products are multiples of 2^-18 below 2^18 and a 32-term sum
+    fits in 41 bits of a float64 mantissa, whatever the order.  Block sums are
+    scaled by 2^(sa + sb) (exact) and added in ascending block order in
+    float64; the total is rounded once to float32.  Returns float32 [n, N].
     """
     n, Kd = aq.shape
     N = wq.shape[0]
     assert Kd % BLOCK == 0, "GEMM operands need whole 32-blocks"
     nb = Kd // BLOCK
     av = _E4M3_VALUES[aq].reshape(n, nb, BLOCK)
-    wv = _E4M3_VALUES[wq].reshape(N, nb, BLOCK)
+    wv = weight_values(wq, w_format).reshape(N, nb, BLOCK)
     sa = e8m0_decode(as_flat[:, :nb])            # [n, nb]
     sw = e8m0_decode(ws_flat[:, :nb])            # [N, nb]
     acc = np.zeros((n, N))
@@ -168,7 +182,7 @@ def silu_mul_ref(g, u):
     return (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
 
 
-def gmm_swiglu_mxquant_ref(aq, as_, w13q, w13s, group_list, group_list_type, I):
+def gmm_swiglu_mxquant_ref(aq, as_, w13q, w13s, group_list, group_list_type, I, w_format="e4m3"):
     """GEMM1 with SwiGLU and MX requant fused, per expert.
 
     For expert e and its rows: acc = A . W13_e^T (R16), gate = acc[:, :I],
@@ -178,7 +192,7 @@ def gmm_swiglu_mxquant_ref(aq, as_, w13q, w13s, group_list, group_list_type, I):
     """
     M, K = aq.shape
     E = w13q.shape[0]
-    assert w13q.shape == (E, 2 * I, K)
+    assert w13q.shape == (E, 2 * I, K if w_format == "e4m3" else K // 2)
     starts, ends = group_bounds(group_list, group_list_type, M)
     as_flat = scales_flat(as_, K)
     h = np.zeros((M, I), np.float32)
@@ -186,16 +200,17 @@ def gmm_swiglu_mxquant_ref(aq, as_, w13q, w13s, group_list, group_list_type, I):
         r0, r1 = starts[e], ends[e]
         if r1 == r0:
             continue
-        acc = _mx_dot(aq[r0:r1], as_flat[r0:r1], w13q[e], scales_flat(w13s[e], K))
+        acc = _mx_dot(aq[r0:r1], as_flat[r0:r1], w13q[e], scales_flat(w13s[e], K), w_format)
         h[r0:r1] = silu_mul_ref(acc[:, :I], acc[:, I:])
     hq, hs = mx_quantize_ref(h.astype(np.float64))
     return hq, hs, h
 
 
-def gmm_mx_ref(aq, as_, wq, ws, group_list, group_list_type):
+def gmm_mx_ref(aq, as_, wq, ws, group_list, group_list_type, w_format="e4m3"):
     """Grouped MX GEMM with bf16 output (GEMM2), per expert.
 
-    y[rows of e] = bf16(A_e . W_e^T) (R16, R17).  wq [E, N, Kd].
+    y[rows of e] = bf16(A_e . W_e^T) (R16, R17).  wq [E, N, Kd] e4m3, or
+    [E, N, Kd/2] packed e2m1 (W4A8).
     Returns bf16 bits uint16 [M, N].
     """
     M, Kd = aq.shape
@@ -207,7 +222,7 @@ def gmm_mx_ref(aq, as_, wq, ws, group_list, group_list_type):
         r0, r1 = starts[e], ends[e]
         if r1 == r0:
             continue
-        y[r0:r1] = _mx_dot(aq[r0:r1], as_flat[r0:r1], wq[e], scales_flat(ws[e], Kd))
+        y[r0:r1] = _mx_dot(aq[r0:r1], as_flat[r0:r1], wq[e], scales_flat(ws[e], Kd), w_format)
     return f32_to_bf16(y)
 
 
@@ -235,23 +250,25 @@ def finalize_ref(y_bf16, topk_w, expanded_row_idx):
 # the whole layer
 # --------------------------------------------------------------------------
 
-def moe_forward_ref(x_bf16, topk_ids, topk_w, w13q, w13s, w2q, w2s):
-    """Route+quant -> GEMM1+SwiGLU+requant -> GEMM2 -> finalize.
+def moe_forward_ref(x_bf16, topk_ids, topk_w, w13q, w13s, w2q, w2s, w_format="e4m3"):
+    """Route+quant -> GEMM1+SwiGLU+requant -> GEMM2 -> finalize.  Weights
+    are e4m3, or packed e2m1 for the W4A8 path (activations MXFP8 either way).
 
     Returns a dict with every intermediate (xq, xs, sorted_row,
     expanded_row_idx, counts, hq, hs, h, y) and the output ``out`` (bf16 bits).
     """
-    E, twoI, K = w13q.shape
+    E, twoI = w13q.shape[:2]
+    K = np.asarray(x_bf16).shape[1]
     I = twoI // 2
     xq, xs, sorted_row, eri, counts = route_quant_ref(x_bf16, topk_ids, E)
-    hq, hs, h = gmm_swiglu_mxquant_ref(xq, xs, w13q, w13s, counts, 1, I)
-    y = gmm_mx_ref(hq, hs, w2q, w2s, counts, 1)
+    hq, hs, h = gmm_swiglu_mxquant_ref(xq, xs, w13q, w13s, counts, 1, I, w_format)
+    y = gmm_mx_ref(hq, hs, w2q, w2s, counts, 1, w_format)
     out = finalize_ref(y, topk_w, eri)
     return dict(xq=xq, xs=xs, sorted_row=sorted_row, expanded_row_idx=eri,
                 counts=counts, hq=hq, hs=hs, h=h, y=y, out=out)
 
 
-def moe_token_ref(x_row_bf16, ids_row, w_row, w13q, w13s, w2q, w2s):
+def moe_token_ref(x_row_bf16, ids_row, w_row, w13q, w13s, w2q, w2s, w_format="e4m3"):
     """One token through the layer with no permutation (brute force).
 
     For each of the token's k experts: MX-quantise the token row, GEMM1 row
@@ -260,17 +277,18 @@ def moe_token_ref(x_row_bf16, ids_row, w_row, w13q, w13s, w2q, w2s):
     so it must reproduce it exactly (the pipeline's batching and permutation
     change no arithmetic).  Returns (out bf16 bits [K], per-j dict list).
     """
-    E, twoI, K = w13q.shape
+    E, twoI = w13q.shape[:2]
+    K = np.asarray(x_row_bf16).size
     I = twoI // 2
     x = bf16_to_f64(np.asarray(x_row_bf16).reshape(1, K))
     xq, xs = mx_quantize_ref(x)
     per = []
     ys = []
     for j, e in enumerate(np.asarray(ids_row).tolist()):
-        acc = _mx_dot(xq, scales_flat(xs, K), w13q[e], scales_flat(w13s[e], K))
+        acc = _mx_dot(xq, scales_flat(xs, K), w13q[e], scales_flat(w13s[e], K), w_format)
         h = silu_mul_ref(acc[:, :I], acc[:, I:])
         hq, hs = mx_quantize_ref(h.astype(np.float64))
-        yv = _mx_dot(hq, scales_flat(hs, I), w2q[e], scales_flat(w2s[e], I))
+        yv = _mx_dot(hq, scales_flat(hs, I), w2q[e], scales_flat(w2s[e], I), w_format)
         yb = f32_to_bf16(yv)
         ys.append(yb[0])
         per.append(dict(expert=e, xq=xq[0], xs=xs[0], h=h[0], hq=hq[0], hs=hs[0], y=yb[0]))
@@ -279,11 +297,11 @@ def moe_token_ref(x_row_bf16, ids_row, w_row, w13q, w13s, w2q, w2s):
     return out[0], per
 
 
-def moe_dense_bruteforce_ref(x_bf16, topk_ids, topk_w, w13q, w13s, w2q, w2s):
+def moe_dense_bruteforce_ref(x_bf16, topk_ids, topk_w, w13q, w13s, w2q, w2s, w_format="e4m3"):
     """Every token through ``moe_token_ref``; tiny inputs only."""
     T = np.asarray(x_bf16).shape[0]
     return np.stack([
-        moe_token_ref(x_bf16[t], topk_ids[t], topk_w[t], w13q, w13s, w2q, w2s)[0]
+        moe_token_ref(x_bf16[t], topk_ids[t], topk_w[t], w13q, w13s, w2q, w2s, w_format)[0]
         for t in range(T)])
 
 

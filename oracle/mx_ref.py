@@ -28,6 +28,20 @@ Readings of points the pages leave open (numbered as in the design notes):
       encodes as 0x80.
 * R7  e4m3 subnormals are kept.
 
+MXFP4 weights (the W4A8 path): "Quantization on Ascend", W4A8 implementation
+notes: weights packed FP4 (float4_e2m1fn_x2, two nibbles per byte) with a
+UE8M0 shared exponent per block of 32; activations stay MXFP8.
+
+* R29 e2m1 is 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit, no
+      infinities or NaN: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (the OCP
+      e2m1 definition; the pages name the dtype only).
+* R30 two codes per byte, element 2i in the low nibble, 2i+1 in the high
+      nibble (the x2 dtype's order).
+* R31 the MXFP4 scale exponent is floor(log2(amax)) - 2 (2 = e2m1's largest
+      exponent), clamped to [-127, 127]; elements round to nearest, ties to
+      even code, saturating at +-6, sign kept (a negative that rounds to 0
+      gives code 8).
+
 Everything is computed in float64 on exact values; no step depends on
 summation order.
 """
@@ -38,6 +52,8 @@ BLOCK = 32            # elements per MX block
 E4M3_MAX = 448.0      # largest finite e4m3 magnitude (S.1111.110)
 E4M3_EMAX = 8         # exponent of the largest e4m3 binade
 E8M0_BIAS = 127       # scale byte = exponent + 127
+E2M1_MAX = 6.0        # largest e2m1 magnitude
+E2M1_EMAX = 2         # exponent of the largest e2m1 binade
 
 
 # --------------------------------------------------------------------------
@@ -190,3 +206,89 @@ def scales_flat(s, kd):
     s = np.asarray(s)
     R = s.shape[0]
     return s.reshape(R, -1)[:, : -(-kd // BLOCK)]
+
+
+# --------------------------------------------------------------------------
+# e2m1 and MXFP4 (weights of the W4A8 path; R29-R31)
+# --------------------------------------------------------------------------
+
+def e2m1_decode(codes):
+    """e2m1 code (0..15) -> value (R29): exponent field 0 is subnormal
+    (m * 0.5), otherwise 2^(e - 1) * (1 + m / 2); bit 3 is the sign."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, np.exp2(e - 1.0) * (1.0 + 0.5 * m))
+    return sign * mag
+
+
+def e2m1_encode(v):
+    """Nearest e2m1 code to each value, ties to the even code, magnitudes
+    above 6 saturate to 6, sign kept (R31)."""
+    v = np.asarray(v, dtype=np.float64)
+    grid = e2m1_decode(np.arange(8))                 # 0, .5, 1, 1.5, 2, 3, 4, 6
+    a = np.minimum(np.abs(v), E2M1_MAX)
+    d = np.abs(a[..., None] - grid)                  # distance to every grid point
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best                                 # one or two nearest points
+    even = cand & ((np.arange(8) % 2) == 0)
+    code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    return (code | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def block_scale_exponent_fp4(amax):
+    """MXFP4 shared exponent (R31): floor(log2 amax) - 2 clamped to
+    [-127, 127]; an all-zero block gets -127 (scale byte 0)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    e = np.full(amax.shape, -127, np.int64)
+    nz = amax > 0
+    e[nz] = np.floor(np.log2(amax[nz])).astype(np.int64) - E2M1_EMAX
+    return np.clip(e, -127, 127)
+
+
+def fp4_pack(codes):
+    """[R, Kd] codes (Kd even) -> [R, Kd/2] bytes, element 2i low nibble (R30)."""
+    c = np.asarray(codes).astype(np.uint8)
+    assert c.shape[-1] % 2 == 0
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def fp4_unpack(q):
+    """[R, Kd/2] bytes -> [R, Kd] codes (R30)."""
+    q = np.asarray(q).astype(np.uint8)
+    out = np.empty(q.shape[:-1] + (2 * q.shape[-1],), np.uint8)
+    out[..., 0::2] = q & 15
+    out[..., 1::2] = q >> 4
+    return out
+
+
+def mxfp4_quantize_ref(v):
+    """MXFP4-quantise each row of v [R, Kd] (Kd even): per block of 32, the
+    shared exponent s (R31), scale byte s + 127, codes e2m1_encode(v * 2^-s)
+    packed two per byte (R30).  Scales [R, ceil(Kd/64), 2] as for MXFP8.
+
+    Returns (q uint8 [R, Kd/2], s uint8 [R, ceil(Kd/64), 2]).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    R, Kd = v.shape
+    assert Kd % 2 == 0, "two codes per byte"
+    nb = -(-Kd // BLOCK)
+    pad = nb * BLOCK - Kd
+    vp = np.concatenate([v, np.zeros((R, pad))], axis=1) if pad else v
+    blocks = vp.reshape(R, nb, BLOCK)
+    s = block_scale_exponent_fp4(np.max(np.abs(blocks), axis=2))
+    codes = e2m1_encode(blocks * np.exp2(-s.astype(np.float64))[:, :, None]).reshape(R, nb * BLOCK)[:, :Kd]
+    sb = (s + E8M0_BIAS).astype(np.uint8)
+    if nb % 2:
+        sb = np.concatenate([sb, np.zeros((R, 1), np.uint8)], axis=1)
+    return fp4_pack(codes), sb.reshape(R, sb.shape[1] // 2, 2)
+
+
+def mxfp4_dequantize_ref(q, s):
+    """e2m1 value times 2^(scale byte - 127).  q [R, Kd/2]; returns [R, Kd]."""
+    codes = fp4_unpack(q)
+    R, Kd = codes.shape
+    nb = -(-Kd // BLOCK)
+    scale = e8m0_decode(np.asarray(s).reshape(R, -1)[:, :nb])
+    return e2m1_decode(codes) * np.repeat(scale, BLOCK, axis=1)[:, :Kd]
