@@ -15,6 +15,9 @@
  *   moe_router          top-k softmax router over a bf16 gate (upstream of
  *                       the layer: produces the ids and weights it takes)
  *   mx_linear           dense MXFP8 linear layer (activation quant + MX GEMM)
+ *   mx_quantize_fp4     MXFP4 (e2m1) quantiser for the W4A8 path's weights
+ *   gmm_swiglu_mxquant_w4a8, gmm_mx_w4a8, moe_w4a8_forward
+ *                       the GEMMs and the layer with MXFP4 expert weights
  *
  * Formats.  MXFP8 = e4m3 payload bytes plus one e8m0 scale byte (exponent +
  * 127, value 2^(byte-127)) per 32 consecutive elements along the reduction
@@ -100,6 +103,20 @@ typedef enum mx_status {
 int mx_quantize(const void* x_bf16, int64_t rows, int64_t kd, int64_t ld,
                 void* q_u8, void* s_u8, void* stream);
 
+/*
+ * MXFP4-quantise `rows` rows of `kd` bf16 elements (row stride `ld`) into
+ * packed e2m1 codes q [rows, kd/2] (element 2i in the low nibble of byte i)
+ * and e8m0 scales s [rows, ceil(kd/64), 2]: the weights of the W4A8 path
+ * ("Quantization on Ascend", W4A8 implementation notes: weights packed FP4,
+ * float4_e2m1fn_x2, two nibbles per byte, one UE8M0 scale per 32 elements;
+ * activations stay MXFP8).  Per 32-block: s = floor(log2(amax)) - 2 clamped
+ * to [-127, 127] (byte s + 127, an all-zero block gets 0), codes = nearest of
+ * +-{0, .5, 1, 1.5, 2, 3, 4, 6} to x * 2^-s, ties to the even code,
+ * saturating at 6, sign kept.  kd % 32 == 0 (MX_ERR_UNSUPPORTED otherwise).
+ */
+int mx_quantize_fp4(const void* x_bf16, int64_t rows, int64_t kd, int64_t ld,
+                    void* q_u8, void* s_u8, void* stream);
+
 /* Workspace bytes moe_route_quant needs for T tokens, top-k, E experts. */
 size_t moe_route_quant_workspace_size(int64_t T, int64_t k, int64_t E);
 
@@ -166,6 +183,26 @@ int moe_finalize(const void* y_bf16, const float* topk_w,
                  const int32_t* expanded_row_idx, int64_t T, int64_t K,
                  int64_t k, int64_t M, void* out_bf16, void* stream);
 
+/*
+ * W4A8 variants ("Quantization on Ascend", W4A8 implementation notes: expert
+ * weights packed FP4 with a UE8M0 scale per 32 elements, activations per-token
+ * MXFP8).  Same arguments, semantics, limits and errors as gmm_swiglu_mxquant
+ * and gmm_mx, except that the weight payload is packed e2m1 (mx_quantize_fp4):
+ *   w13 uint8 [E, 2I, K/2] (gate rows [0, I), up rows [I, 2I)),
+ *   w   uint8 [E, N, Kd/2]; element 2c in the low nibble of byte c.
+ * Scales keep the [.., K/64, 2] layout.  GEMM1's output hq/hs stays MXFP8.
+ */
+int gmm_swiglu_mxquant_w4a8(const void* a_u8, const void* a_s,
+                            const void* w13_u8, const void* w13_s,
+                            const int64_t* group_list, int group_list_type,
+                            int64_t M, int64_t K, int64_t I, int64_t E,
+                            void* hq_u8, void* hs_u8, float* h_f32_debug,
+                            void* stream);
+int gmm_mx_w4a8(const void* a_u8, const void* a_s, const void* w_u8, const void* w_s,
+                const int64_t* group_list, int group_list_type,
+                int64_t M, int64_t N, int64_t Kd, int64_t E,
+                void* y_bf16, void* stream);
+
 /* Workspace bytes moe_mxfp8_forward needs (holds every intermediate). */
 size_t moe_mxfp8_forward_workspace_size(int64_t T, int64_t K, int64_t I,
                                         int64_t E, int64_t k);
@@ -182,6 +219,18 @@ int moe_mxfp8_forward(const void* x_bf16, const int32_t* topk_ids,
                       int64_t T, int64_t K, int64_t I, int64_t E, int64_t k,
                       void* out_bf16, void* workspace, size_t ws_bytes,
                       void* stream);
+
+/*
+ * The whole layer with MXFP4 expert weights (the W4A8 path): as
+ * moe_mxfp8_forward with w13 uint8 [E, 2I, K/2] and w2 uint8 [E, K, I/2]
+ * packed e2m1 (see gmm_swiglu_mxquant_w4a8); same workspace and layout.
+ */
+int moe_w4a8_forward(const void* x_bf16, const int32_t* topk_ids,
+                     const float* topk_w, const void* w13_u8,
+                     const void* w13_s, const void* w2_u8, const void* w2_s,
+                     int64_t T, int64_t K, int64_t I, int64_t E, int64_t k,
+                     void* out_bf16, void* workspace, size_t ws_bytes,
+                     void* stream);
 
 /* Byte offsets of the intermediates inside the forward workspace, so a caller
  * can inspect them after the stream has run.  Fills the 8 offsets in order:

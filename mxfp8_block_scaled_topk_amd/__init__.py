@@ -21,7 +21,7 @@ __all__ = [
     "MxError", "lib_path", "load", "mx_quantize", "moe_route_quant", "gmm_swiglu_mxquant",
     "gmm_mx", "moe_finalize", "moe_mxfp8_forward", "forward_workspace", "forward_intermediates",
     "route_workspace_size", "forward_workspace_size", "last_error", "moe_router", "mx_linear",
-    "linear_workspace_size",
+    "linear_workspace_size", "mx_quantize_fp4", "gmm_mx_w4a8", "gmm_swiglu_mxquant_w4a8", "moe_w4a8_forward",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,10 +54,14 @@ def load():
     P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     sig = {
         "mx_quantize": (I32, [P, I64, I64, I64, P, P, P]),
+        "mx_quantize_fp4": (I32, [P, I64, I64, I64, P, P, P]),
         "moe_route_quant_workspace_size": (SZ, [I64, I64, I64]),
         "moe_route_quant": (I32, [P, P, I64, I64, I64, I64, P, P, P, P, P, P, SZ, P]),
         "gmm_swiglu_mxquant": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P, P, P]),
         "gmm_mx": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]),
+        "gmm_mx_w4a8": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]),
+        "gmm_swiglu_mxquant_w4a8": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P, P, P]),
+        "moe_w4a8_forward": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
         "moe_finalize": (I32, [P, P, P, I64, I64, I64, I64, P, P]),
         "moe_mxfp8_forward_workspace_size": (SZ, [I64, I64, I64, I64, I64]),
         "moe_mxfp8_forward": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
@@ -201,18 +205,19 @@ def moe_route_quant(x, topk_ids, E, out=None, workspace=None, stream=None):
 
 
 def gmm_swiglu_mxquant(a, a_s, w13, w13_s, group_list, group_list_type=GROUP_COUNT, out=None,
-                       h_debug=False, stream=None):
+                       h_debug=False, stream=None, _w4=False):
     """GEMM1 + SwiGLU + MX requant.  Returns (hq, hs) or (hq, hs, h) with h_debug."""
     _need(a, torch.uint8, "a", 2); _need(w13, torch.uint8, "w13", 3)
     M, K = a.shape
     E, twoI, Kw = w13.shape
-    if Kw != K or twoI % 2:
-        raise ValueError(f"w13 must be [E, 2I, {K}], got {tuple(w13.shape)}")
+    Kb = K // 2 if _w4 else K           # weight payload bytes per row
+    if Kw != Kb or twoI % 2:
+        raise ValueError(f"w13 must be [E, 2I, {Kb}], got {tuple(w13.shape)}")
     I = twoI // 2
     dev = a.device
     _need_shape(a, (M, K), "a", torch.uint8, dev)
     _need_shape(a_s, (M, _pairs(K), 2), "a_s", torch.uint8, dev)
-    _need_shape(w13, (E, twoI, K), "w13", torch.uint8, dev)
+    _need_shape(w13, (E, twoI, Kb), "w13", torch.uint8, dev)
     _need_shape(w13_s, (E, twoI, _pairs(K), 2), "w13_s", torch.uint8, dev)
     _need_shape(group_list, (E,), "group_list", torch.int64, dev)
     if out is None:
@@ -223,32 +228,35 @@ def gmm_swiglu_mxquant(a, a_s, w13, w13_s, group_list, group_list_type=GROUP_COU
     _need_shape(hs, (M, _pairs(I), 2), "hs", torch.uint8, dev)
     h = torch.empty((M, I), dtype=torch.float32, device=dev) if h_debug else None
     _need_gpu(a, "a")
-    rc = load().gmm_swiglu_mxquant(_ptr(a), _ptr(a_s), _ptr(w13), _ptr(w13_s), _ptr(group_list),
-                                   group_list_type, M, K, I, E, _ptr(hq), _ptr(hs), _ptr(h), _stream(stream))
-    _check(rc, "gmm_swiglu_mxquant")
+    fn = load().gmm_swiglu_mxquant_w4a8 if _w4 else load().gmm_swiglu_mxquant
+    rc = fn(_ptr(a), _ptr(a_s), _ptr(w13), _ptr(w13_s), _ptr(group_list), group_list_type, M, K, I, E, _ptr(hq),
+            _ptr(hs), _ptr(h), _stream(stream))
+    _check(rc, "gmm_swiglu_mxquant_w4a8" if _w4 else "gmm_swiglu_mxquant")
     return (hq, hs, h) if h_debug else (hq, hs)
 
 
-def gmm_mx(a, a_s, w, w_s, group_list, group_list_type=GROUP_COUNT, out=None, stream=None):
+def gmm_mx(a, a_s, w, w_s, group_list, group_list_type=GROUP_COUNT, out=None, stream=None, _w4=False):
     """Grouped MX GEMM, bf16 output [M, N]."""
     _need(a, torch.uint8, "a", 2); _need(w, torch.uint8, "w", 3)
     M, Kd = a.shape
     E, N, Kw = w.shape
-    if Kw != Kd:
-        raise ValueError(f"w must be [E, N, {Kd}], got {tuple(w.shape)}")
+    Kb = Kd // 2 if _w4 else Kd
+    if Kw != Kb:
+        raise ValueError(f"w must be [E, N, {Kb}], got {tuple(w.shape)}")
     dev = a.device
     _need_shape(a, (M, Kd), "a", torch.uint8, dev)
     _need_shape(a_s, (M, _pairs(Kd), 2), "a_s", torch.uint8, dev)
-    _need_shape(w, (E, N, Kd), "w", torch.uint8, dev)
+    _need_shape(w, (E, N, Kb), "w", torch.uint8, dev)
     _need_shape(w_s, (E, N, _pairs(Kd), 2), "w_s", torch.uint8, dev)
     _need_shape(group_list, (E,), "group_list", torch.int64, dev)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _need_shape(out, (M, N), "out", torch.bfloat16, dev)
     _need_gpu(a, "a")
-    rc = load().gmm_mx(_ptr(a), _ptr(a_s), _ptr(w), _ptr(w_s), _ptr(group_list), group_list_type, M, N, Kd, E,
-                       _ptr(out), _stream(stream))
-    _check(rc, "gmm_mx")
+    fn = load().gmm_mx_w4a8 if _w4 else load().gmm_mx
+    rc = fn(_ptr(a), _ptr(a_s), _ptr(w), _ptr(w_s), _ptr(group_list), group_list_type, M, N, Kd, E, _ptr(out),
+            _stream(stream))
+    _check(rc, "gmm_mx_w4a8" if _w4 else "gmm_mx")
     return out
 
 
@@ -282,7 +290,8 @@ def forward_workspace(T, K, I, E, k, device="cuda"):
     return torch.empty(max(forward_workspace_size(T, K, I, E, k), 256), dtype=torch.uint8, device=device)
 
 
-def moe_mxfp8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, workspace=None, stream=None):
+def moe_mxfp8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, workspace=None, stream=None,
+                      _w4=False):
     """The whole layer.  x [T,K] bf16, topk_ids [T,k] i32, topk_w [T,k] f32,
     w13 [E,2I,K] u8 + w13_s [E,2I,K/64,2], w2 [E,K,I] u8 + w2_s [E,K,I/64,2].
     Returns out [T,K] bf16."""
@@ -291,16 +300,17 @@ def moe_mxfp8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, works
     T, K = x.shape
     k = topk_ids.shape[1]
     E, twoI, Kw = w13.shape
-    if Kw != K or twoI % 2:
-        raise ValueError(f"w13 must be [E, 2I, {K}], got {tuple(w13.shape)}")
+    Kb = K // 2 if _w4 else K
+    if Kw != Kb or twoI % 2:
+        raise ValueError(f"w13 must be [E, 2I, {Kb}], got {tuple(w13.shape)}")
     I = twoI // 2
     dev = x.device
     _need_shape(x, (T, K), "x", torch.bfloat16, dev)
     _need_shape(topk_ids, (T, k), "topk_ids", torch.int32, dev)
     _need_shape(topk_w, (T, k), "topk_w", torch.float32, dev)
-    _need_shape(w13, (E, twoI, K), "w13", torch.uint8, dev)
+    _need_shape(w13, (E, twoI, Kb), "w13", torch.uint8, dev)
     _need_shape(w13_s, (E, twoI, _pairs(K), 2), "w13_s", torch.uint8, dev)
-    _need_shape(w2, (E, K, I), "w2", torch.uint8, dev)
+    _need_shape(w2, (E, K, I // 2 if _w4 else I), "w2", torch.uint8, dev)
     _need_shape(w2_s, (E, K, _pairs(I), 2), "w2_s", torch.uint8, dev)
     if out is None:
         out = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
@@ -310,10 +320,10 @@ def moe_mxfp8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, works
         workspace = forward_workspace(T, K, I, E, k, dev)
     _need_workspace(workspace, need, dev)
     _need_gpu(x, "x")
-    rc = load().moe_mxfp8_forward(_ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w13), _ptr(w13_s), _ptr(w2),
-                                  _ptr(w2_s), T, K, I, E, k, _ptr(out), _ptr(workspace), workspace.numel(),
-                                  _stream(stream))
-    _check(rc, "moe_mxfp8_forward")
+    fn = load().moe_w4a8_forward if _w4 else load().moe_mxfp8_forward
+    rc = fn(_ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w13), _ptr(w13_s), _ptr(w2), _ptr(w2_s), T, K, I, E, k,
+            _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "moe_w4a8_forward" if _w4 else "moe_mxfp8_forward")
     return out
 
 
@@ -391,3 +401,45 @@ def mx_linear(x, w, w_s, out=None, workspace=None, stream=None):
                           _stream(stream))
     _check(rc, "mx_linear")
     return out
+
+
+def mx_quantize_fp4(x, q=None, s=None, stream=None):
+    """MXFP4-quantise the last dim of a bf16 tensor [..., Kd] (Kd % 32 == 0).
+    Returns (q uint8 [..., Kd/2] packed e2m1, s uint8 [..., ceil(Kd/64), 2])."""
+    _need(x, torch.bfloat16, "x")
+    kd = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    x2 = x.reshape(-1, kd) if x.dim() != 2 else x
+    if x2.stride(-1) != 1:
+        raise ValueError("x must have unit stride along the last dim")
+    if kd % 2:
+        raise ValueError("Kd must be even (two codes per byte)")
+    rows = x2.shape[0]
+    if q is None:
+        q = torch.empty(lead + (kd // 2,), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty(lead + (_pairs(kd), 2), dtype=torch.uint8, device=x.device)
+    _need_shape(q, lead + (kd // 2,), "q", torch.uint8, x.device)
+    _need_shape(s, lead + (_pairs(kd), 2), "s", torch.uint8, x.device)
+    ld = x2.stride(0) if rows > 1 else kd
+    _need_gpu(x, "x")
+    rc = load().mx_quantize_fp4(_ptr(x2), rows, kd, ld, _ptr(q), _ptr(s), _stream(stream))
+    _check(rc, "mx_quantize_fp4")
+    return q, s
+
+
+def gmm_swiglu_mxquant_w4a8(a, a_s, w13, w13_s, group_list, group_list_type=GROUP_COUNT, out=None,
+                            h_debug=False, stream=None):
+    """GEMM1 + SwiGLU + MX requant with MXFP4 weights: w13 [E, 2I, K/2] packed
+    e2m1 + w13_s [E, 2I, K/64, 2].  Returns (hq, hs) (MXFP8) or (hq, hs, h)."""
+    return gmm_swiglu_mxquant(a, a_s, w13, w13_s, group_list, group_list_type, out, h_debug, stream, _w4=True)
+
+
+def gmm_mx_w4a8(a, a_s, w, w_s, group_list, group_list_type=GROUP_COUNT, out=None, stream=None):
+    """Grouped MX GEMM with MXFP4 weights (w [E, N, Kd/2] packed e2m1), bf16 [M, N]."""
+    return gmm_mx(a, a_s, w, w_s, group_list, group_list_type, out, stream, _w4=True)
+
+
+def moe_w4a8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, workspace=None, stream=None):
+    """The layer with MXFP4 expert weights: w13 [E,2I,K/2], w2 [E,K,I/2] packed e2m1."""
+    return moe_mxfp8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out, workspace, stream, _w4=True)

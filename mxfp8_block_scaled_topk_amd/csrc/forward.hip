@@ -17,9 +17,10 @@ int launch_route_quant(const uint16_t* x, const int32_t* ids, int64_t T, int64_t
 int check_gmm_common(const char* name, int gl_type, int64_t M, int64_t Kd, int64_t E);
 int launch_gmm_swiglu(const uint8_t* a, const uint8_t* as, const uint8_t* w13, const uint8_t* w13s,
                       const int64_t* gl, int gl_type, int64_t M, int64_t K, int64_t I, int64_t E, uint8_t* hq,
-                      uint8_t* hs, float* hdbg, hipStream_t stream);
+                      uint8_t* hs, float* hdbg, hipStream_t stream, bool w4);
 int launch_gmm_mx(const uint8_t* a, const uint8_t* as, const uint8_t* w, const uint8_t* ws, const int64_t* gl,
-                  int gl_type, int64_t M, int64_t N, int64_t Kd, int64_t E, uint16_t* y, hipStream_t stream);
+                  int gl_type, int64_t M, int64_t N, int64_t Kd, int64_t E, uint16_t* y, hipStream_t stream,
+                  bool w4);
 int launch_finalize(const uint16_t* y, const float* w, const int32_t* eri, int64_t T, int64_t K, int64_t k,
                     int64_t M, uint16_t* out, hipStream_t stream);
 
@@ -83,25 +84,28 @@ extern "C" int moe_mxfp8_forward_workspace_layout(int64_t T, int64_t K, int64_t 
   return MX_OK;
 }
 
-extern "C" int moe_mxfp8_forward(const void* x_bf16, const int32_t* topk_ids, const float* topk_w,
-                                 const void* w13_u8, const void* w13_s, const void* w2_u8, const void* w2_s,
-                                 int64_t T, int64_t K, int64_t I, int64_t E, int64_t k, void* out_bf16,
-                                 void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+
+// The layer on one stream; w4: the expert weights are MXFP4 (packed e2m1,
+// the W4A8 path), the activations are MXFP8 either way.
+int forward(const char* name, bool w4, const void* x_bf16, const int32_t* topk_ids, const float* topk_w,
+            const void* w13_u8, const void* w13_s, const void* w2_u8, const void* w2_s, int64_t T, int64_t K,
+            int64_t I, int64_t E, int64_t k, void* out_bf16, void* workspace, size_t ws_bytes, void* stream) {
   using namespace mxmoe;
   int rc = check_forward_args(T, K, I, E, k);
   if (rc) return rc;
-  if (!workspace) return fail(MX_ERR_INVALID_ARG, "moe_mxfp8_forward: null workspace");
+  if (!workspace) return fail(MX_ERR_INVALID_ARG, "%s: null workspace", name);
   if (T > 0 && (!x_bf16 || !topk_ids || !topk_w || !w13_u8 || !w13_s || !w2_u8 || !w2_s || !out_bf16))
-    return fail(MX_ERR_INVALID_ARG, "moe_mxfp8_forward: null pointer");
+    return fail(MX_ERR_INVALID_ARG, "%s: null pointer", name);
   const Layout L = layout(T, K, I, E, k);
   if (ws_bytes < L.total)
-    return fail(MX_ERR_WORKSPACE, "moe_mxfp8_forward: workspace %zu bytes < %zu needed", ws_bytes, L.total);
+    return fail(MX_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", name, ws_bytes, L.total);
   const uintptr_t align_or = reinterpret_cast<uintptr_t>(x_bf16) | reinterpret_cast<uintptr_t>(w13_u8) |
                              reinterpret_cast<uintptr_t>(w2_u8) | reinterpret_cast<uintptr_t>(out_bf16) |
                              reinterpret_cast<uintptr_t>(workspace);
   const uintptr_t align_s = reinterpret_cast<uintptr_t>(w13_s) | reinterpret_cast<uintptr_t>(w2_s);
   if (align_or % 16 || align_s % 4)
-    return fail(MX_ERR_UNSUPPORTED, "moe_mxfp8_forward: misaligned pointer");
+    return fail(MX_ERR_UNSUPPORTED, "%s: misaligned pointer", name);
   if (T == 0) return MX_OK;
   hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
@@ -119,10 +123,28 @@ extern "C" int moe_mxfp8_forward(const void* x_bf16, const int32_t* topk_ids, co
                           rws, s);
   if (rc) return rc;
   rc = launch_gmm_swiglu(xq, xs, static_cast<const uint8_t*>(w13_u8), static_cast<const uint8_t*>(w13_s), gl, 1, M,
-                         K, I, E, hq, hs, nullptr, s);
+                         K, I, E, hq, hs, nullptr, s, w4);
   if (rc) return rc;
   rc = launch_gmm_mx(hq, hs, static_cast<const uint8_t*>(w2_u8), static_cast<const uint8_t*>(w2_s), gl, 1, M, K, I,
-                     E, y, s);
+                     E, y, s, w4);
   if (rc) return rc;
   return launch_finalize(y, topk_w, eri, T, K, k, M, static_cast<uint16_t*>(out_bf16), s);
+}
+
+}  // namespace
+
+extern "C" int moe_mxfp8_forward(const void* x_bf16, const int32_t* topk_ids, const float* topk_w,
+                                 const void* w13_u8, const void* w13_s, const void* w2_u8, const void* w2_s,
+                                 int64_t T, int64_t K, int64_t I, int64_t E, int64_t k, void* out_bf16,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  return forward("moe_mxfp8_forward", false, x_bf16, topk_ids, topk_w, w13_u8, w13_s, w2_u8, w2_s, T, K, I, E, k,
+                 out_bf16, workspace, ws_bytes, stream);
+}
+
+extern "C" int moe_w4a8_forward(const void* x_bf16, const int32_t* topk_ids, const float* topk_w,
+                                const void* w13_u8, const void* w13_s, const void* w2_u8, const void* w2_s,
+                                int64_t T, int64_t K, int64_t I, int64_t E, int64_t k, void* out_bf16,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  return forward("moe_w4a8_forward", true, x_bf16, topk_ids, topk_w, w13_u8, w13_s, w2_u8, w2_s, T, K, I, E, k,
+                 out_bf16, workspace, ws_bytes, stream);
 }

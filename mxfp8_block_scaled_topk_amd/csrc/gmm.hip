@@ -177,8 +177,13 @@ struct TileInfo {
 // Physical 16-byte chunk of logical chunk c in tile row r (128-byte rows).
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <bool kSwiglu>
+// kW4: the weights are MXFP4 (packed e2m1, Kd/2 bytes per row, the W4A8
+// path); the token operand stays MXFP8.
+template <bool kSwiglu, bool kW4>
 __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
+  constexpr int kNA = kW4 ? 2 : 4;          // weight DMAs per wave per stage
+  constexpr int kDmaOps = kNA + 5;          // + 4 token rows + 1 scale load
+  constexpr int kRowA = kW4 ? SK / 2 : SK;  // weight bytes per LDS row per stage
   __shared__ __attribute__((aligned(16))) Stage st[kSlots];
   __shared__ int s_tile0[kMaxE + 1];
   __shared__ int s_row0[kMaxE + 1];
@@ -319,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       sbase = (int64_t)ti.nt * BN + 64 * (wave & 3);
     }
     const int64_t wr = (int64_t)ti.e * p.Nw;
-    s.wrow = uniptr(p.w + (wr + wbase) * Kd);
+    s.wrow = uniptr(p.w + (wr + wbase) * (kW4 ? Kd / 2 : Kd));
     s.arow = uniptr(p.a + ti.m0 * Kd);
     s.srowp = wave < 4 ? uniptr(p.ws + (wr + sbase) * srow) : uniptr(p.as + ti.m0 * srow);
     s.last = uni((int)std::min<int64_t>(p.M - 1 - ti.m0, BM - 1));
@@ -334,6 +339,9 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   };
   // per-lane parts of the DMA offsets
   const uint32_t lane_off_even = (uint32_t)(drow * Kd + dch_even * 16);
+  // e2m1 weights: 64-byte row pieces, an instruction fills 16 rows; lane l at
+  // row l/4, physical chunk l%4 = logical chunk (l%4) ^ ((row/4)%4)
+  const uint32_t lane_off_a4 = (uint32_t)((lane >> 2) * (Kd / 2) + ((((lane & 3) ^ ((lane >> 4) & 3))) << 4));
   const uint32_t lane_off_odd = (uint32_t)(drow * Kd + dch_odd * 16);
   const uint32_t lane_s = (uint32_t)(lane * srow);
   // scale fetch: waves 0-3 weight scales (64 rows from srowp), waves 4-7
@@ -359,11 +367,16 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     const uint32_t ko = (uint32_t)(kr * SK);
     // the row and k offsets go into the per-lane 32-bit offset, so the only
     // scalar operand is the row base
-    if (i < 4) {
-      dma16(((i & 1) ? lane_off_odd : lane_off_even) + (uint32_t)(8 * i * Kd) + ko, src.wrow,
-            base + (uint32_t)offsetof(Stage, a) + (uint32_t)((32 * wave + 8 * i) * SK));
-    } else if (i < 8) {
-      const int j = i - 4;
+    if (i < kNA) {
+      if constexpr (kW4) {
+        dma16(lane_off_a4 + (uint32_t)(8 * i * Kd) + (uint32_t)(kr * (SK / 2)), src.wrow,
+              base + (uint32_t)offsetof(Stage, a) + (uint32_t)((32 * wave + 16 * i) * (SK / 2)));
+      } else {
+        dma16(((i & 1) ? lane_off_odd : lane_off_even) + (uint32_t)(8 * i * Kd) + ko, src.wrow,
+              base + (uint32_t)offsetof(Stage, a) + (uint32_t)((32 * wave + 8 * i) * SK));
+      }
+    } else if (i < kNA + 4) {
+      const int j = i - kNA;
       // rows past M repeat the last row
       const uint32_t row = std::min(b_row0 + (uint32_t)(8 * j * Kd), (uint32_t)(src.last * Kd));
       const uint32_t voff = row + (uint32_t)(((j & 1) ? dch_odd : dch_even) * 16) + ko;
@@ -374,13 +387,13 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   };
   auto dma_stage = [&](const Src& src, int ks, int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kDmaPerStage; ++i) dma_part(i, src, ks, slot);
+    for (int i = 0; i < kDmaOps; ++i) dma_part(i, src, ks, slot);
   };
 
   // ---- LDS read addresses: row (li) part and the swizzled chunk parts ------
   // Fragment rows differ by multiples of 32, so (row/2)%8 = (li/2)%8 for all.
   const int sw = (li >> 1) & 7;
-  const uint32_t rd_a = (uint32_t)offsetof(Stage, a) + (uint32_t)((128 * wn + li) * SK);
+  const uint32_t rd_a = (uint32_t)offsetof(Stage, a) + (uint32_t)((128 * wn + li) * kRowA);
   const uint32_t rd_b = (uint32_t)offsetof(Stage, b) + (uint32_t)((64 * wm + li) * SK);
   const uint32_t rd_sa = (uint32_t)offsetof(Stage, sa) + (uint32_t)((128 * wn + li) * 4);
   const uint32_t rd_sb = (uint32_t)offsetof(Stage, sb) + (uint32_t)((64 * wm + li) * 4);
@@ -396,12 +409,24 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     asm("" : "+s"(b));   // opaque: one add per load instead of both slots' addresses kept live
     return (const lds_u8*)(uintptr_t)b;
   };
+  // e2m1 fragment of sub-step s: lane group g holds the 32 codes of k block
+  // g (k [64s + 32g, +32)), i.e. bytes [32s + 16g, +16) of the row's piece:
+  // logical chunk 2s + lg, stored at (2s + lg) ^ ((row/4)%4); (row/4)%4 =
+  // (li/4)%4 for every fragment row
+  uint32_t chk4[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) chk4[c] = (uint32_t)(((2 * c + lg) ^ ((li >> 2) & 3)) << 4);
   auto load_a = [&](int slot, int s, int f, v8i& frag, int& sc) __attribute__((always_inline)) {
     const lds_u8* S = slot_ptr(slot);
-    const lds_u8* pa = S + rd_a + f * 32 * SK;
-    const u32x4 a0 = *reinterpret_cast<lds_u32x4_v*>(pa + chk[2 * s]);
-    const u32x4 a1 = *reinterpret_cast<lds_u32x4_v*>(pa + chk[2 * s + 1]);
-    frag = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    const lds_u8* pa = S + rd_a + f * 32 * kRowA;
+    if constexpr (kW4) {
+      const u32x4 a0 = *reinterpret_cast<lds_u32x4_v*>(pa + chk4[s]);
+      frag = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
+    } else {
+      const u32x4 a0 = *reinterpret_cast<lds_u32x4_v*>(pa + chk[2 * s]);
+      const u32x4 a1 = *reinterpret_cast<lds_u32x4_v*>(pa + chk[2 * s + 1]);
+      frag = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    }
     sc = (int)*reinterpret_cast<lds_u8_v*>(S + rd_sa + f * 128 + 2 * s + lg);
   };
   auto load_b = [&](int slot, int s, int f, v8i& frag, int& sc) __attribute__((always_inline)) {
@@ -452,7 +477,8 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int fm = m >> 2, fn = m & 3;
-        acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[fn], fb[fm], acc[fn][fm], 0, 0, 0,
+        // A format 4 = e2m1 (W4A8), 0 = e4m3; B (tokens) is always e4m3
+        acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[fn], fb[fm], acc[fn][fm], kW4 ? 4 : 0, 0, 0,
                                                                        sa[fn], 0, sb[fm]);
         // pin the MFMA here: without a use at this point the optimiser sinks
         // the (side-effect free) MFMAs below the loads that were meant to
@@ -511,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
           }
           if (m == 1) {
 #pragma unroll
-            for (int i = 5; i < kDmaPerStage; ++i) dma_part(i, t, tks, slot);
+            for (int i = 5; i < kDmaOps; ++i) dma_part(i, t, tks, slot);
           }
         });
       } else {
@@ -644,7 +670,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   wait_vmcnt0();
 }
 
-template <bool kSwiglu>
+template <bool kSwiglu, bool kW4>
 int launch(const GmmParams& p, hipStream_t stream, const char* name) {
   if (p.M == 0) return MX_OK;
   const int64_t upper = ((p.M + BM - 1) / BM + p.E) * (int64_t)p.n_tiles;
@@ -652,7 +678,7 @@ int launch(const GmmParams& p, hipStream_t stream, const char* name) {
   int64_t grid = (int64_t)num_cus() / 8 * 8;
   if (grid < 8) grid = 8;
   if (grid > (upper + 7) / 8 * 8) grid = (upper + 7) / 8 * 8;
-  gmm_kernel<kSwiglu><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+  gmm_kernel<kSwiglu, kW4><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
   return check_launch(name);
 }
 
@@ -674,63 +700,99 @@ int check_gmm_common(const char* name, int gl_type, int64_t M, int64_t Kd, int64
 
 int launch_gmm_mx(const uint8_t* a, const uint8_t* as, const uint8_t* w, const uint8_t* ws,
                   const int64_t* gl, int gl_type, int64_t M, int64_t N, int64_t Kd, int64_t E, uint16_t* y,
-                  hipStream_t stream) {
+                  hipStream_t stream, bool w4) {
   GmmParams p{};
   p.a = a; p.as = as; p.w = w; p.ws = ws; p.group_list = gl; p.gl_type = gl_type;
   p.E = (int)E; p.M = M; p.Kd = Kd; p.Nw = N; p.n_tiles = (int)(N / BN); p.y = y;
-  return launch<false>(p, stream, "gmm_mx");
+  return w4 ? launch<false, true>(p, stream, "gmm_mx_w4a8") : launch<false, false>(p, stream, "gmm_mx");
 }
 
 int launch_gmm_swiglu(const uint8_t* a, const uint8_t* as, const uint8_t* w13, const uint8_t* w13s,
                       const int64_t* gl, int gl_type, int64_t M, int64_t K, int64_t I, int64_t E, uint8_t* hq,
-                      uint8_t* hs, float* hdbg, hipStream_t stream) {
+                      uint8_t* hs, float* hdbg, hipStream_t stream, bool w4) {
   GmmParams p{};
   p.a = a; p.as = as; p.w = w13; p.ws = w13s; p.group_list = gl; p.gl_type = gl_type;
   p.E = (int)E; p.M = M; p.Kd = K; p.Nw = 2 * I; p.n_tiles = (int)(I / (BN / 2)); p.I = I;
   p.hq = hq; p.hs = hs; p.hdbg = hdbg;
-  return launch<true>(p, stream, "gmm_swiglu_mxquant");
+  return w4 ? launch<true, true>(p, stream, "gmm_swiglu_mxquant_w4a8")
+            : launch<true, false>(p, stream, "gmm_swiglu_mxquant");
 }
 
 }  // namespace mxmoe
 
-extern "C" int gmm_mx(const void* a_u8, const void* a_s, const void* w_u8, const void* w_s,
-                      const int64_t* group_list, int group_list_type, int64_t M, int64_t N, int64_t Kd,
-                      int64_t E, void* y_bf16, void* stream) {
+namespace {
+
+// Host checks shared by the e4m3 and e2m1 (W4A8) entry points of GEMM2.
+int gmm_mx_entry(const char* name, bool w4, const void* a_u8, const void* a_s, const void* w_u8, const void* w_s,
+                 const int64_t* group_list, int group_list_type, int64_t M, int64_t N, int64_t Kd, int64_t E,
+                 void* y_bf16, void* stream) {
   using namespace mxmoe;
-  int rc = check_gmm_common("gmm_mx", group_list_type, M, Kd, E);
+  int rc = check_gmm_common(name, group_list_type, M, Kd, E);
   if (rc) return rc;
-  if (N <= 0) return fail(MX_ERR_INVALID_ARG, "gmm_mx: bad N=%lld", (long long)N);
-  if (N % BN != 0) return fail(MX_ERR_UNSUPPORTED, "gmm_mx: N=%lld is not a multiple of %d", (long long)N, BN);
+  if (N <= 0) return fail(MX_ERR_INVALID_ARG, "%s: bad N=%lld", name, (long long)N);
+  if (N % BN != 0) return fail(MX_ERR_UNSUPPORTED, "%s: N=%lld is not a multiple of %d", name, (long long)N, BN);
   if (!group_list || (M > 0 && (!a_u8 || !a_s || !w_u8 || !w_s || !y_bf16)))
-    return fail(MX_ERR_INVALID_ARG, "gmm_mx: null pointer");
+    return fail(MX_ERR_INVALID_ARG, "%s: null pointer", name);
   if (reinterpret_cast<uintptr_t>(a_u8) % 16 || reinterpret_cast<uintptr_t>(w_u8) % 16 ||
       reinterpret_cast<uintptr_t>(a_s) % 4 || reinterpret_cast<uintptr_t>(w_s) % 4 ||
       reinterpret_cast<uintptr_t>(y_bf16) % 16)
-    return fail(MX_ERR_UNSUPPORTED, "gmm_mx: misaligned pointer");
+    return fail(MX_ERR_UNSUPPORTED, "%s: misaligned pointer", name);
   return launch_gmm_mx(static_cast<const uint8_t*>(a_u8), static_cast<const uint8_t*>(a_s),
                        static_cast<const uint8_t*>(w_u8), static_cast<const uint8_t*>(w_s), group_list,
-                       group_list_type, M, N, Kd, E, static_cast<uint16_t*>(y_bf16), as_stream(stream));
+                       group_list_type, M, N, Kd, E, static_cast<uint16_t*>(y_bf16), as_stream(stream), w4);
+}
+
+// Host checks shared by the e4m3 and e2m1 (W4A8) entry points of GEMM1.
+int gmm_swiglu_entry(const char* name, bool w4, const void* a_u8, const void* a_s, const void* w13_u8,
+                     const void* w13_s, const int64_t* group_list, int group_list_type, int64_t M, int64_t K,
+                     int64_t I, int64_t E, void* hq_u8, void* hs_u8, float* h_f32_debug, void* stream) {
+  using namespace mxmoe;
+  int rc = check_gmm_common(name, group_list_type, M, K, E);
+  if (rc) return rc;
+  if (I <= 0) return fail(MX_ERR_INVALID_ARG, "%s: bad I=%lld", name, (long long)I);
+  if (I % (BN / 2) != 0)
+    return fail(MX_ERR_UNSUPPORTED, "%s: I=%lld is not a multiple of %d", name, (long long)I, BN / 2);
+  if (!group_list || (M > 0 && (!a_u8 || !a_s || !w13_u8 || !w13_s || !hq_u8 || !hs_u8)))
+    return fail(MX_ERR_INVALID_ARG, "%s: null pointer", name);
+  if (reinterpret_cast<uintptr_t>(a_u8) % 16 || reinterpret_cast<uintptr_t>(w13_u8) % 16 ||
+      reinterpret_cast<uintptr_t>(a_s) % 4 || reinterpret_cast<uintptr_t>(w13_s) % 4 ||
+      reinterpret_cast<uintptr_t>(hq_u8) % 16 || reinterpret_cast<uintptr_t>(hs_u8) % 4 ||
+      reinterpret_cast<uintptr_t>(h_f32_debug) % 16)
+    return fail(MX_ERR_UNSUPPORTED, "%s: misaligned pointer", name);
+  return launch_gmm_swiglu(static_cast<const uint8_t*>(a_u8), static_cast<const uint8_t*>(a_s),
+                           static_cast<const uint8_t*>(w13_u8), static_cast<const uint8_t*>(w13_s), group_list,
+                           group_list_type, M, K, I, E, static_cast<uint8_t*>(hq_u8),
+                           static_cast<uint8_t*>(hs_u8), h_f32_debug, as_stream(stream), w4);
+}
+
+}  // namespace
+
+extern "C" int gmm_mx(const void* a_u8, const void* a_s, const void* w_u8, const void* w_s,
+                      const int64_t* group_list, int group_list_type, int64_t M, int64_t N, int64_t Kd,
+                      int64_t E, void* y_bf16, void* stream) {
+  return gmm_mx_entry("gmm_mx", false, a_u8, a_s, w_u8, w_s, group_list, group_list_type, M, N, Kd, E, y_bf16,
+                      stream);
+}
+
+extern "C" int gmm_mx_w4a8(const void* a_u8, const void* a_s, const void* w_u8, const void* w_s,
+                           const int64_t* group_list, int group_list_type, int64_t M, int64_t N, int64_t Kd,
+                           int64_t E, void* y_bf16, void* stream) {
+  return gmm_mx_entry("gmm_mx_w4a8", true, a_u8, a_s, w_u8, w_s, group_list, group_list_type, M, N, Kd, E,
+                      y_bf16, stream);
 }
 
 extern "C" int gmm_swiglu_mxquant(const void* a_u8, const void* a_s, const void* w13_u8, const void* w13_s,
                                   const int64_t* group_list, int group_list_type, int64_t M, int64_t K,
                                   int64_t I, int64_t E, void* hq_u8, void* hs_u8, float* h_f32_debug,
                                   void* stream) {
-  using namespace mxmoe;
-  int rc = check_gmm_common("gmm_swiglu_mxquant", group_list_type, M, K, E);
-  if (rc) return rc;
-  if (I <= 0) return fail(MX_ERR_INVALID_ARG, "gmm_swiglu_mxquant: bad I=%lld", (long long)I);
-  if (I % (BN / 2) != 0)
-    return fail(MX_ERR_UNSUPPORTED, "gmm_swiglu_mxquant: I=%lld is not a multiple of %d", (long long)I, BN / 2);
-  if (!group_list || (M > 0 && (!a_u8 || !a_s || !w13_u8 || !w13_s || !hq_u8 || !hs_u8)))
-    return fail(MX_ERR_INVALID_ARG, "gmm_swiglu_mxquant: null pointer");
-  if (reinterpret_cast<uintptr_t>(a_u8) % 16 || reinterpret_cast<uintptr_t>(w13_u8) % 16 ||
-      reinterpret_cast<uintptr_t>(a_s) % 4 || reinterpret_cast<uintptr_t>(w13_s) % 4 ||
-      reinterpret_cast<uintptr_t>(hq_u8) % 16 || reinterpret_cast<uintptr_t>(hs_u8) % 4 ||
-      reinterpret_cast<uintptr_t>(h_f32_debug) % 16)
-    return fail(MX_ERR_UNSUPPORTED, "gmm_swiglu_mxquant: misaligned pointer");
-  return launch_gmm_swiglu(static_cast<const uint8_t*>(a_u8), static_cast<const uint8_t*>(a_s),
-                           static_cast<const uint8_t*>(w13_u8), static_cast<const uint8_t*>(w13_s), group_list,
-                           group_list_type, M, K, I, E, static_cast<uint8_t*>(hq_u8),
-                           static_cast<uint8_t*>(hs_u8), h_f32_debug, as_stream(stream));
+  return gmm_swiglu_entry("gmm_swiglu_mxquant", false, a_u8, a_s, w13_u8, w13_s, group_list, group_list_type, M,
+                          K, I, E, hq_u8, hs_u8, h_f32_debug, stream);
+}
+
+extern "C" int gmm_swiglu_mxquant_w4a8(const void* a_u8, const void* a_s, const void* w13_u8, const void* w13_s,
+                                       const int64_t* group_list, int group_list_type, int64_t M, int64_t K,
+                                       int64_t I, int64_t E, void* hq_u8, void* hs_u8, float* h_f32_debug,
+                                       void* stream) {
+  return gmm_swiglu_entry("gmm_swiglu_mxquant_w4a8", true, a_u8, a_s, w13_u8, w13_s, group_list,
+                          group_list_type, M, K, I, E, hq_u8, hs_u8, h_f32_debug, stream);
 }

@@ -62,7 +62,92 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_any(
   }
 }
 
+// ---- MXFP4 (e2m1) weights of the W4A8 path ------------------------------------
+// ("Quantization on Ascend", W4A8 implementation notes: weights packed FP4,
+// two e2m1 codes per byte, one UE8M0 scale per 32 elements.)  Scale exponent
+// floor(log2 amax) - 2 (e2m1's largest binade is 2^2), i.e. the byte is the
+// amax's biased exponent field minus 2, floored at 0 (the clamp at -127).
+// Codes: nearest of 0, .5, 1, 1.5, 2, 3, 4, 6, ties to the even code,
+// saturating at 6, sign kept; element 2i in the low nibble.
+
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+  const float a = fabsf(x);
+  // midpoints between neighbouring magnitudes; ">=" where the upper
+  // neighbour has the even code, ">" where the lower one has
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | (__float_as_uint(x) >> 31 << 3);
+}
+
+__device__ __forceinline__ uint32_t mxfp4_block32(const float (&v)[32], uint32_t (&q)[4]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int field = static_cast<int>(__float_as_uint(amax) >> 23);
+  const uint32_t sb = static_cast<uint32_t>(field > 2 ? field - 2 : 0);
+  const float inv = e8m0_inverse(sb);   // 2^-s, exact scaling
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) word |= e2m1_code(v[8 * w + j] * inv) << (4 * j);
+    q[w] = word;
+  }
+  return sb;
+}
+
+// kd % 32 == 0.  kVec: ld % 8 == 0 and x 16-byte aligned (16-byte loads) and
+// q 16-byte aligned (one 16-byte store per block).
+template <bool kVec>
+__global__ __launch_bounds__(kThreads) void mx_quantize_fp4_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t kd, int64_t ld,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int64_t nb = kd / 32;
+  const int64_t s_stride = ((nb + 1) / 2) * 2;
+  const int64_t total = rows * nb;
+  for (int64_t blk = blockIdx.x * (int64_t)kThreads + threadIdx.x; blk < total;
+       blk += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = blk / nb, c = blk - r * nb;
+    float v[32];
+    if constexpr (kVec) {
+      const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + c * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) unpack_bf16x8(src[i], v + 8 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(x[r * ld + c * 32 + i]);
+    }
+    uint32_t w[4];
+    const uint32_t sb = mxfp4_block32(v, w);
+    uint8_t* dst = q + r * (kd / 2) + c * 16;
+    if constexpr (kVec) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[i] = static_cast<uint8_t>(w[i >> 2] >> (8 * (i & 3)));
+    }
+    s[r * s_stride + c] = static_cast<uint8_t>(sb);
+    if ((nb & 1) && c == nb - 1) s[r * s_stride + nb] = 0;
+  }
+}
+
 }  // namespace
+
+int launch_mx_quantize_fp4(const uint16_t* x, int64_t rows, int64_t kd, int64_t ld, uint8_t* q, uint8_t* s,
+                           hipStream_t stream) {
+  const int64_t total = rows * (kd / 32);
+  if (total == 0) return MX_OK;
+  int64_t grid = (total + kThreads - 1) / kThreads;
+  const int64_t cap = (int64_t)num_cus() * 16;
+  if (grid > cap) grid = cap;
+  const bool vec = (ld % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(q) % 16 == 0);
+  if (vec)
+    mx_quantize_fp4_kernel<true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(x, rows, kd, ld, q, s);
+  else
+    mx_quantize_fp4_kernel<false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(x, rows, kd, ld, q, s);
+  return check_launch("mx_quantize_fp4");
+}
 
 int launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t kd, int64_t ld,
                        uint8_t* q, uint8_t* s, hipStream_t stream) {
@@ -94,4 +179,17 @@ extern "C" int mx_quantize(const void* x_bf16, int64_t rows, int64_t kd, int64_t
   return launch_mx_quantize(static_cast<const uint16_t*>(x_bf16), rows, kd, ld,
                             static_cast<uint8_t*>(q_u8), static_cast<uint8_t*>(s_u8),
                             as_stream(stream));
+}
+
+extern "C" int mx_quantize_fp4(const void* x_bf16, int64_t rows, int64_t kd, int64_t ld,
+                               void* q_u8, void* s_u8, void* stream) {
+  using namespace mxmoe;
+  if (!x_bf16 || !q_u8 || !s_u8) return fail(MX_ERR_INVALID_ARG, "mx_quantize_fp4: null pointer");
+  if (rows < 0 || kd <= 0 || ld < kd)
+    return fail(MX_ERR_INVALID_ARG, "mx_quantize_fp4: bad sizes rows=%lld kd=%lld ld=%lld",
+                (long long)rows, (long long)kd, (long long)ld);
+  if (kd % 32 != 0)
+    return fail(MX_ERR_UNSUPPORTED, "mx_quantize_fp4: kd=%lld is not a multiple of 32", (long long)kd);
+  return launch_mx_quantize_fp4(static_cast<const uint16_t*>(x_bf16), rows, kd, ld,
+                                static_cast<uint8_t*>(q_u8), static_cast<uint8_t*>(s_u8), as_stream(stream));
 }

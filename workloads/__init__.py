@@ -31,7 +31,7 @@ import numpy as np
 import torch
 
 _TAGS = {"x": 1, "gate": 2, "w13": 3, "w2": 4, "outlier": 5, "bias": 6,
-         "w13q": 7, "w13s": 8, "w2q": 9, "w2s": 10}
+         "w13q": 7, "w13s": 8, "w2q": 9, "w2s": 10, "w13q4": 11, "w13s4": 12, "w2q4": 13, "w2s4": 14}
 
 
 @dataclass(frozen=True)
@@ -244,3 +244,23 @@ def dense_linear_inputs(T, K, N, seed=0):
     x = normal_bf16(rng_for(seed, "x"), (T, K), 1.0, chunk_rows=4096)
     wq, ws = _offline_checkpoint(rng_for(seed, "w2q"), rng_for(seed, "w2s"), (N, K))
     return x, wq, ws
+
+
+def _offline_checkpoint_fp4(rng_q, rng_s, shape):
+    """Pre-quantised MXFP4 weights (the W4A8 path) as a checkpoint ships them:
+    packed e2m1 codes, two per byte, each code uniform over the 16 codes;
+    scale bytes uniform over {120, 121, 122} (2^-7 .. 2^-5) in the pair-split
+    [..., K/64, 2] layout, so magnitudes fall in about [4e-3, 0.19]."""
+    *lead, Kd = shape
+    q = rng_q.integers(0, 256, size=tuple(lead) + (Kd // 2,), dtype=np.uint8)
+    s = rng_s.integers(120, 123, size=tuple(lead) + (Kd // 64, 2), dtype=np.uint8)
+    return q, s
+
+
+def make_weights_w4a8(cfg, seed=0):
+    """Checkpoint-style MXFP4 expert weights for the W4A8 path:
+    w13q4 [E, 2I, K/2], w13s4 [E, 2I, K/64, 2], w2q4 [E, K, I/2], w2s4."""
+    E, K, I = cfg.E, cfg.K, cfg.I
+    w13q, w13s = _offline_checkpoint_fp4(rng_for(seed, "w13q4"), rng_for(seed, "w13s4"), (E, 2 * I, K))
+    w2q, w2s = _offline_checkpoint_fp4(rng_for(seed, "w2q4"), rng_for(seed, "w2s4"), (E, K, I))
+    return dict(w13q4=w13q, w13s4=w13s, w2q4=w2q, w2s4=w2s)
