@@ -18,7 +18,8 @@ object is computed from those.  The top-k router upstream of the layer
 "in_step": false: the layer takes the ids and weights as inputs.  So is a
 dense MXFP8 linear layer (mx_linear, T=16384, K=N=4096, offline-style
 pre-quantised weight): a second workload of the same MX GEMM, not part of
-the MoE step.
+the MoE step.  And so is the same 16K prefill layer with MXFP4 (e2m1) expert
+weights (moe_w4a8_forward), with its two GEMMs timed separately.
 """
 
 import argparse
@@ -34,7 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import mxfp8_block_scaled_topk_amd as mx  # noqa: E402
-from workloads import CONFIGS, dense_linear_inputs, make_inputs, router_inputs  # noqa: E402
+from workloads import CONFIGS, dense_linear_inputs, make_inputs, make_weights_w4a8, router_inputs  # noqa: E402
 
 MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8/MXFP8 MFMA
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
@@ -211,6 +212,44 @@ def main():
                                "hbm_GBs": round(l_bytes / l_dur / 1e9, 1), "alg_bytes": int(l_bytes),
                                "alg_flops": int(l_flops), "in_step": False}
     del lx, lwq, lws, ly, lws_buf
+
+    # ---- the same layer with MXFP4 (e2m1) expert weights (W4A8) -------------
+    # The mixed e2m1 x e4m3 block-scaled MFMA issues at the fp8 rate, so the
+    # fraction is taken against the fp8 peak.
+    w4 = {n: torch.from_numpy(v).to(dev) for n, v in make_weights_w4a8(cfg).items()}
+    hq4, hs4, y4 = torch.empty_like(inter["hq"]), torch.empty_like(inter["hs"]), torch.empty_like(inter["y"])
+
+    def step_w4():
+        mx.moe_w4a8_forward(x, ids, w, w4["w13q4"], w4["w13s4"], w4["w2q4"], w4["w2s4"], out=out, workspace=ws)
+
+    for _ in range(3):
+        step_w4()
+    rev[0].record(stream)
+    for _ in range(args.steps):
+        step_w4()
+    rev[1].record(stream)
+    torch.cuda.synchronize()
+    f4_dur = rev[0].elapsed_time(rev[1]) * 1e-3 / args.steps
+    mx.moe_route_quant(x, ids, E, out=route_out, workspace=rws)
+    ev4 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        e = ev4[s]
+        e[0].record(stream)
+        mx.gmm_swiglu_mxquant_w4a8(inter["xq"], inter["xs"], w4["w13q4"], w4["w13s4"], inter["group_list"], 1,
+                                   out=(hq4, hs4))
+        e[1].record(stream)
+        mx.gmm_mx_w4a8(hq4, hs4, w4["w2q4"], w4["w2s4"], inter["group_list"], 1, out=y4)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    w4k = {}
+    for i, n in enumerate(["gemm1_swiglu_requant", "gemm2"]):
+        t = float(np.mean([ev4[s][i].elapsed_time(ev4[s][i + 1]) for s in range(args.steps)])) * 1e-3
+        tf = alg[n]["flops"] / t / 1e12
+        w4k[n] = {"avg_us": round(t * 1e6, 2), "TFLOPs": round(tf, 1),
+                  "mfma_frac": round(tf / MFMA_FP8_PEAK_TFLOPS, 4)}
+    kernels["w4a8_layer"] = {"avg_us": round(f4_dur * 1e6, 2), "tokens_per_s": round(T / f4_dur, 1),
+                             "weights": "e2m1 + e8m0 per 32", "gemms": w4k, "in_step": False}
+    del w4, hq4, hs4, y4
 
     g1, g2 = alg["gemm1_swiglu_requant"], alg["gemm2"]
     gemm_tflops = (g1["flops"] + g2["flops"]) / (dur["gemm1_swiglu_requant"] + dur["gemm2"]) / 1e12
