@@ -25,7 +25,11 @@
 // Data movement.  K advances 128 bytes per stage through a two-slot LDS ring
 // (66 KB per slot: 256 rows x 128 B of each operand plus the u32 of 4 scale
 // bytes per row), filled by direct global->LDS loads (global_load_lds_dwordx4
-// / _dword, 1 KB per instruction, no staging registers).  Whole 128-byte rows
+// / _dword, 1 KB per instruction, no staging registers).  When the k stages
+// divide into groups of 4, the scales instead come 16 bytes per row (4
+// stages) at a time into a small double-buffered ring of their own: a scale
+// row is 1/32 of an operand row, so per-stage dword loads touch a line for
+// every two rows and made up a third of all line requests.  Whole 128-byte rows
 // matter: measured on gfx950, 64-byte row pieces halve the L2->LDS rate.  The
 // loads are issued from inline assembly with explicit vmcnt accounting (the
 // compiler otherwise waits for every outstanding LDS DMA before any LDS
@@ -179,14 +183,24 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // kW4: the weights are MXFP4 (packed e2m1, Kd/2 bytes per row, the W4A8
 // path); the token operand stays MXFP8.
-template <bool kSwiglu, bool kW4>
+// kG: k stages per scale load.  kG = 1: every stage's DMA brings the 4 scale
+// bytes per row of that stage (a 64-lane dword load touches 32 lines for
+// 256 bytes).  kG = 4 (k stages a multiple of 4, scale rows 16-byte
+// aligned): the first stage of each group of 4 brings 16 bytes per row into
+// a separate double-buffered scale ring, a quarter of the line requests
+// (measured: scale requests cost GEMM1 about a tenth of its time at kG = 1).
+template <bool kSwiglu, bool kW4, int kG>
 __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
+  static_assert(kG == 1 || kG == 4, "scale groups of 1 or 4 stages");
   constexpr int kNA = kW4 ? 2 : 4;          // weight DMAs per wave per stage
   constexpr int kDmaOps = kNA + 5;          // + 4 token rows + 1 scale load
   constexpr int kRowA = kW4 ? SK / 2 : SK;  // weight bytes per LDS row per stage
   __shared__ __attribute__((aligned(16))) Stage st[kSlots];
   __shared__ int s_tile0[kMaxE + 1];
   __shared__ int s_row0[kMaxE + 1];
+  // kG = 4: scale words of 4 consecutive stages; group buffer (g/4)%2 holds
+  // 256 weight rows then 256 token rows, 16 bytes per row
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[kG == 4 ? 2 * 2 * 256 * 4 : 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -333,7 +347,10 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     // rows (same nt) or token rows (same mt) reach each 128-byte k slice at
     // different times, so one of them takes the L2 miss and the others hit
     // (measured: GEMM2 17 % faster, GEMM1 3 %, at the 16K prefill size).
-    // The accumulation order changes with it, deterministically per tile.
+    // With scale groups (kG = 4) the groups of 4 stages are visited in an
+    // order rotated by rot/4 and the stages inside each group rotated by
+    // rot%4, so every group is still fetched whole at its first stage.  The
+    // accumulation order changes with it, deterministically per tile.
     s.rot = uni((int)((ti.nt + (ti.m0 - s_row0[ti.e]) / BM) % nk));
     return s;
   };
@@ -358,12 +375,27 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   // token rows of this wave's B part: row 32 wave + 8 j + drow, as a byte offset
   const uint32_t b_row0 = (uint32_t)((32 * wave + drow) * Kd);
   const uint32_t st_base = lds_addr(&st[0]);
+  const uint32_t sc_base = lds_addr(&s_sc[0]);
+  // memory k stage of tile stage ks for a tile with rotation rot
+  const int n_groups = nk / kG;
+  auto kmem = [&](int ks, int rot) __attribute__((always_inline)) -> int {
+    if constexpr (kG == 1) {
+      const int kr = ks + rot;
+      return kr >= nk ? kr - nk : kr;
+    } else {
+      int grp = (ks >> 2) + (rot >> 2);
+      grp = grp >= n_groups ? grp - n_groups : grp;
+      return 4 * grp + (((ks & 3) + rot) & 3);
+    }
+  };
+  int cur_r = 0;   // rot % 4 of the tile whose fragments are being read
+  const uint32_t s_lds4 = wave < 4 ? (uint32_t)(1024 * wave) : (uint32_t)(4096 + 1024 * (wave - 4));
   // One DMA instruction of k stage ks of the tile whose source is `src`,
-  // into ring slot `slot`: i = 0..3 weight rows, 4..7 token rows, 8 scales.
-  auto dma_part = [&](int i, const Src& src, int ks, int slot) __attribute__((always_inline)) {
-    const uint32_t base = st_base + (uint32_t)slot * (uint32_t)sizeof(Stage);
-    int kr = ks + src.rot;   // the k stage in memory
-    kr = kr >= nk ? kr - nk : kr;
+  // global stage gs (ring slot gs%2): i = 0..3 weight rows, 4..7 token rows,
+  // 8 scales.
+  auto dma_part = [&](int i, const Src& src, int ks, int gs) __attribute__((always_inline)) {
+    const uint32_t base = st_base + (uint32_t)(gs & 1) * (uint32_t)sizeof(Stage);
+    const int kr = kmem(ks, src.rot);   // the k stage in memory
     const uint32_t ko = (uint32_t)(kr * SK);
     // the row and k offsets go into the per-lane 32-bit offset, so the only
     // scalar operand is the row base
@@ -381,13 +413,17 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       const uint32_t row = std::min(b_row0 + (uint32_t)(8 * j * Kd), (uint32_t)(src.last * Kd));
       const uint32_t voff = row + (uint32_t)(((j & 1) ? dch_odd : dch_even) * 16) + ko;
       dma16(voff, src.arow, base + (uint32_t)offsetof(Stage, b) + (uint32_t)((32 * wave + 8 * j) * SK));
-    } else {
+    } else if constexpr (kG == 1) {
       dma4(s_voff(src.last) + (uint32_t)(kr * 4), src.srowp, base + s_lds);
+    } else if ((ks & 3) == 0) {
+      // the group's 16 bytes per row, from its first stage in memory
+      dma16(s_voff(src.last) + (uint32_t)((kr & ~3) * 4), src.srowp,
+            sc_base + (uint32_t)(((gs >> 2) & 1) * 8192) + s_lds4);
     }
   };
-  auto dma_stage = [&](const Src& src, int ks, int slot) __attribute__((always_inline)) {
+  auto dma_stage = [&](const Src& src, int ks, int gs) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kDmaOps; ++i) dma_part(i, src, ks, slot);
+    for (int i = 0; i < kDmaOps; ++i) dma_part(i, src, ks, gs);
   };
 
   // ---- LDS read addresses: row (li) part and the swizzled chunk parts ------
@@ -397,6 +433,8 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   const uint32_t rd_b = (uint32_t)offsetof(Stage, b) + (uint32_t)((64 * wm + li) * SK);
   const uint32_t rd_sa = (uint32_t)offsetof(Stage, sa) + (uint32_t)((128 * wn + li) * 4);
   const uint32_t rd_sb = (uint32_t)offsetof(Stage, sb) + (uint32_t)((64 * wm + li) * 4);
+  const uint32_t rd_sa4 = (uint32_t)((128 * wn + li) * 16);          // kG = 4 scale ring
+  const uint32_t rd_sb4 = (uint32_t)(4096 + (64 * wm + li) * 16);
   uint32_t chk[4];   // byte offset of logical chunk 2c + lg within a row
 #pragma unroll
   for (int c = 0; c < 4; ++c) chk[c] = (uint32_t)(((2 * c + lg) ^ sw) << 4);
@@ -416,8 +454,17 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   uint32_t chk4[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) chk4[c] = (uint32_t)(((2 * c + lg) ^ ((li >> 2) & 3)) << 4);
-  auto load_a = [&](int slot, int s, int f, v8i& frag, int& sc) __attribute__((always_inline)) {
-    const lds_u8* S = slot_ptr(slot);
+  // kG = 4: the scale bytes of global stage gs (tile stage ks = gs mod nk,
+  // tiles start at multiples of 4) sit at word (ks + rot) % 4 of each row's
+  // 16 bytes in group buffer (gs/4)%2
+  auto group_ptr = [&](int gs) __attribute__((always_inline)) {
+    uint32_t b = sc_base + (uint32_t)(((gs >> 2) & 1) * 8192 + (((gs & 3) + cur_r) & 3) * 4);
+    asm("" : "+s"(b));
+    return (const lds_u8*)(uintptr_t)b;
+  };
+  // fragments of global stage gs (ring slot gs%2)
+  auto load_a = [&](int gs, int s, int f, v8i& frag, int& sc) __attribute__((always_inline)) {
+    const lds_u8* S = slot_ptr(gs & 1);
     const lds_u8* pa = S + rd_a + f * 32 * kRowA;
     if constexpr (kW4) {
       const u32x4 a0 = *reinterpret_cast<lds_u32x4_v*>(pa + chk4[s]);
@@ -427,15 +474,21 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       const u32x4 a1 = *reinterpret_cast<lds_u32x4_v*>(pa + chk[2 * s + 1]);
       frag = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
     }
-    sc = (int)*reinterpret_cast<lds_u8_v*>(S + rd_sa + f * 128 + 2 * s + lg);
+    if constexpr (kG == 1)
+      sc = (int)*reinterpret_cast<lds_u8_v*>(S + rd_sa + f * 128 + 2 * s + lg);
+    else
+      sc = (int)*reinterpret_cast<lds_u8_v*>(group_ptr(gs) + rd_sa4 + f * 512 + 2 * s + lg);
   };
-  auto load_b = [&](int slot, int s, int f, v8i& frag, int& sc) __attribute__((always_inline)) {
-    const lds_u8* S = slot_ptr(slot);
+  auto load_b = [&](int gs, int s, int f, v8i& frag, int& sc) __attribute__((always_inline)) {
+    const lds_u8* S = slot_ptr(gs & 1);
     const lds_u8* pb = S + rd_b + f * 32 * SK;
     const u32x4 b0 = *reinterpret_cast<lds_u32x4_v*>(pb + chk[2 * s]);
     const u32x4 b1 = *reinterpret_cast<lds_u32x4_v*>(pb + chk[2 * s + 1]);
     frag = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-    sc = (int)*reinterpret_cast<lds_u8_v*>(S + rd_sb + f * 128 + 2 * s + lg);
+    if constexpr (kG == 1)
+      sc = (int)*reinterpret_cast<lds_u8_v*>(S + rd_sb + f * 128 + 2 * s + lg);
+    else
+      sc = (int)*reinterpret_cast<lds_u8_v*>(group_ptr(gs) + rd_sb4 + f * 512 + 2 * s + lg);
   };
   // ---- schedule ---------------------------------------------------------------
   // Stage g (tile-local k stage ks) lives in slot g%2.  Sub-step 0 of stage g
@@ -464,6 +517,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   for (int cj = 0; cj < my_tiles; ++cj) {
     const TileInfo cur = tile_info(cj * TS + xcd_base);
     const Src csrc = make_src(cj * TS + xcd_base);
+    cur_r = csrc.rot & 3;
     const bool has_next = cj + 1 < my_tiles;
     const Src nsrc = has_next ? make_src((cj + 1) * TS + xcd_base) : csrc;
     v8i fa[4], fb[2];
@@ -471,9 +525,9 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     v16f acc[4][2];
     // The 8 MFMAs of one sub-step, B fragment 0 with A fragments 0..3, then B
     // fragment 1 with A 0..3.  Each fragment is reloaded for the next sub-step
-    // (slot `nslot`, sub-step `ns`) right after its last MFMA, so the LDS reads
+    // (stage `nstage`, sub-step `ns`) right after its last MFMA, so the LDS reads
     // overlap the matrix work; `extra(m)` runs after MFMA m (DMA issue).
-    auto substep = [&](int nslot, int ns, auto kReload, auto extra) __attribute__((always_inline)) {
+    auto substep = [&](int nstage, int ns, auto kReload, auto extra) __attribute__((always_inline)) {
   #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int fm = m >> 2, fn = m & 3;
@@ -486,19 +540,19 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
         asm volatile("" : "+v"(acc[fn][fm]));
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (decltype(kReload)::value) {
-          if (m == 3) load_b(nslot, ns, 0, fb[0], sb[0]);
-          if (m >= 4) load_a(nslot, ns, m - 4, fa[m - 4], sa[m - 4]);
-          if (m == 7) load_b(nslot, ns, 1, fb[1], sb[1]);
+          if (m == 3) load_b(nstage, ns, 0, fb[0], sb[0]);
+          if (m >= 4) load_a(nstage, ns, m - 4, fa[m - 4], sa[m - 4]);
+          if (m == 7) load_b(nstage, ns, 1, fb[1], sb[1]);
         }
         extra(m);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    auto load_all = [&](int slot, int s) __attribute__((always_inline)) {
+    auto load_all = [&](int gs, int s) __attribute__((always_inline)) {
   #pragma unroll
-      for (int f = 0; f < 4; ++f) load_a(slot, s, f, fa[f], sa[f]);
+      for (int f = 0; f < 4; ++f) load_a(gs, s, f, fa[f], sa[f]);
   #pragma unroll
-      for (int f = 0; f < 2; ++f) load_b(slot, s, f, fb[f], sb[f]);
+      for (int f = 0; f < 2; ++f) load_b(gs, s, f, fb[f], sb[f]);
     };
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -508,13 +562,12 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
         for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
     // the tile's first fragments (stage g has landed: the prologue's barrier,
     // or the middle barrier of the previous tile's last stage)
-    load_all(g & 1, 0);
+    load_all(g, 0);
 
     // one k stage; kDma: issue stage g+2's DMA (every stage but the tile's last)
     auto stage = [&](int ks, auto kDma) __attribute__((always_inline)) {
-      const int slot = g & 1;
       __builtin_amdgcn_sched_barrier(0);
-      substep(slot, 1, std::true_type{}, [&](int) {});
+      substep(g, 1, std::true_type{}, [&](int) {});
       wait_vmcnt0();   // this wave's part of stage g+1 has landed
       barrier();       // every wave's has, and nobody reads slot g%2 any more
       if constexpr (decltype(kDma)::value) {
@@ -530,18 +583,18 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
         const int tks = in_tile ? ks + 2 : (has_next ? 0 : nk - 1);
         // the DMA goes out early in the sub-step (measured: issuing it over
         // all eight MFMAs leaves the last loads too little time to land)
-        substep(slot ^ 1, 0, std::true_type{}, [&](int m) __attribute__((always_inline)) {
+        substep(g + 1, 0, std::true_type{}, [&](int m) __attribute__((always_inline)) {
           if (m == 0) {
 #pragma unroll
-            for (int i = 0; i < 5; ++i) dma_part(i, t, tks, slot);
+            for (int i = 0; i < 5; ++i) dma_part(i, t, tks, g + 2);
           }
           if (m == 1) {
 #pragma unroll
-            for (int i = 5; i < kDmaOps; ++i) dma_part(i, t, tks, slot);
+            for (int i = 5; i < kDmaOps; ++i) dma_part(i, t, tks, g + 2);
           }
         });
       } else {
-        substep(slot ^ 1, 0, std::false_type{}, [&](int) {});   // the next tile reloads at its start
+        substep(g + 1, 0, std::false_type{}, [&](int) {});   // the next tile reloads at its start
       }
       __builtin_amdgcn_sched_barrier(0);
       ++g;
@@ -588,7 +641,8 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
         uint16_t* y0 = p.y + (cur.m0 + mc0) * N + (int64_t)cur.nt * BN + 128 * wn + 8 * rc;
 #pragma unroll
         for (int it = 0; it < 8; ++it)
-          if (mc0 + 4 * it < cur.rows_valid) *reinterpret_cast<u32x4*>(y0 + 4 * it * N) = v[it];
+          if (mc0 + 4 * it < cur.rows_valid)
+            __builtin_nontemporal_store(v[it], reinterpret_cast<u32x4*>(y0 + 4 * it * N));
         asm volatile("" ::: "memory");   // a wave's LDS accesses execute in issue order
       }
     } else {
@@ -661,9 +715,9 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     // per tile the stage 0 of the tile after next)
     barrier();
     if (nk > 1) {
-      if (has_next) dma_stage(nsrc, 1, (g + 1) & 1);
+      if (has_next) dma_stage(nsrc, 1, g + 1);
     } else if (cj + 2 < my_tiles) {
-      dma_stage(make_src((cj + 2) * TS + xcd_base), 0, (g + 1) & 1);
+      dma_stage(make_src((cj + 2) * TS + xcd_base), 0, g + 1);
     }
   }
   // outstanding DMA must land before the workgroup's LDS is released
@@ -678,7 +732,14 @@ int launch(const GmmParams& p, hipStream_t stream, const char* name) {
   int64_t grid = (int64_t)num_cus() / 8 * 8;
   if (grid < 8) grid = 8;
   if (grid > (upper + 7) / 8 * 8) grid = (upper + 7) / 8 * 8;
-  gmm_kernel<kSwiglu, kW4><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+  // scale groups of 4 stages when the k stages divide into them and both
+  // scale tensors are 16-byte aligned (every scale row then is)
+  const bool groups = (p.Kd / BK) % 4 == 0 && reinterpret_cast<uintptr_t>(p.as) % 16 == 0 &&
+                      reinterpret_cast<uintptr_t>(p.ws) % 16 == 0;
+  if (groups)
+    gmm_kernel<kSwiglu, kW4, 4><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+  else
+    gmm_kernel<kSwiglu, kW4, 1><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
   return check_launch(name);
 }
 
