@@ -320,6 +320,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     const uint8_t* arow;   // token row m0 (uniform)
     const uint8_t* srowp;  // scale row base this wave fetches (uniform)
     int last;              // min(M - 1 - m0, BM - 1): last readable token row of the tile, relative to m0
+    int tok;               // nonzero if this wave's 32 token rows hold a row of the tile's expert
     int rot;               // the tile's k-stage rotation
   };
   auto make_src = [&](int t) __attribute__((always_inline)) -> Src {
@@ -342,6 +343,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     s.arow = uniptr(p.a + ti.m0 * Kd);
     s.srowp = wave < 4 ? uniptr(p.ws + (wr + sbase) * srow) : uniptr(p.as + ti.m0 * srow);
     s.last = uni((int)std::min<int64_t>(p.M - 1 - ti.m0, BM - 1));
+    s.tok = 32 * wave < ti.rows_valid;
     // Tile (expert e, m-tile mt of e, n-tile nt) runs its k stages in the
     // order (nt + mt) % nk, (nt + mt + 1) % nk, ...: tiles that share weight
     // rows (same nt) or token rows (same mt) reach each 128-byte k slice at
@@ -412,7 +414,10 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       // rows past M repeat the last row
       const uint32_t row = std::min(b_row0 + (uint32_t)(8 * j * Kd), (uint32_t)(src.last * Kd));
       const uint32_t voff = row + (uint32_t)(((j & 1) ? dch_odd : dch_even) * 16) + ko;
-      dma16(voff, src.arow, base + (uint32_t)offsetof(Stage, b) + (uint32_t)((32 * wave + 8 * j) * SK));
+      // a ragged tail tile skips token rows past its expert's rows: only the
+      // outputs of those (never stored) rows read what stays in LDS there
+      if (src.tok)
+        dma16(voff, src.arow, base + (uint32_t)offsetof(Stage, b) + (uint32_t)((32 * wave + 8 * j) * SK));
     } else if constexpr (kG == 1) {
       dma4(s_voff(src.last) + (uint32_t)(kr * 4), src.srowp, base + s_lds);
     } else if ((ks & 3) == 0) {
@@ -516,6 +521,10 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   int g = 0;   // global stage index
   for (int cj = 0; cj < my_tiles; ++cj) {
     const TileInfo cur = tile_info(cj * TS + xcd_base);
+    // Ragged tail tiles: a wave whose 64 tokens are all past the expert's
+    // rows computes nothing (no fragment loads, MFMAs or epilogue work); it
+    // still issues its share of the weight DMA and meets every barrier.
+    const bool active = 64 * wm < cur.rows_valid;
     const Src csrc = make_src(cj * TS + xcd_base);
     cur_r = csrc.rot & 3;
     const bool has_next = cj + 1 < my_tiles;
@@ -528,6 +537,11 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     // (stage `nstage`, sub-step `ns`) right after its last MFMA, so the LDS reads
     // overlap the matrix work; `extra(m)` runs after MFMA m (DMA issue).
     auto substep = [&](int nstage, int ns, auto kReload, auto extra) __attribute__((always_inline)) {
+      if (!active) {
+  #pragma unroll
+        for (int m = 0; m < 8; ++m) extra(m);
+        return;
+      }
   #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int fm = m >> 2, fn = m & 3;
@@ -562,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
         for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
     // the tile's first fragments (stage g has landed: the prologue's barrier,
     // or the middle barrier of the previous tile's last stage)
-    load_all(g, 0);
+    if (active) load_all(g, 0);
 
     // one k stage; kDma: issue stage g+2's DMA (every stage but the tile's last)
     auto stage = [&](int ks, auto kDma) __attribute__((always_inline)) {
@@ -579,6 +593,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
         t.arow = in_tile ? csrc.arow : nsrc.arow;
         t.srowp = in_tile ? csrc.srowp : nsrc.srowp;
         t.last = in_tile ? csrc.last : nsrc.last;
+        t.tok = in_tile ? csrc.tok : nsrc.tok;
         t.rot = in_tile ? csrc.rot : nsrc.rot;
         const int tks = in_tile ? ks + 2 : (has_next ? 0 : nk - 1);
         // the DMA goes out early in the sub-step (measured: issuing it over
@@ -613,6 +628,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       // halves swapped when r >= 16, so both the writes (lane = token) and
       // the reads (16 lanes per row) are free of bank conflicts.
       const int64_t N = p.Nw;
+      if (active) {
       const int li = opaque(lane & 31), lg = opaque(lane >> 5), lane_e = opaque(lane);
       lds_u8* stg = (lds_u8*)(uintptr_t)(st_base + (uint32_t)((g - 1) & 1) * (uint32_t)sizeof(Stage) +
                                          (uint32_t)(wave * 8192));
@@ -645,6 +661,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
             __builtin_nontemporal_store(v[it], reinterpret_cast<u32x4*>(y0 + 4 * it * N));
         asm volatile("" ::: "memory");   // a wave's LDS accesses execute in issue order
       }
+      }   // active
     } else {
       // SwiGLU, MX requant, and the stores through LDS: the two waves that
       // share a 64-token block (wn = 0, 1: 64 h columns each) stage their
@@ -657,8 +674,10 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       lds_u8* grp = (lds_u8*)(uintptr_t)(st_base + (uint32_t)((g - 1) & 1) * (uint32_t)sizeof(Stage) +
                                          (uint32_t)(wm * (64 * 128 + 64 * 4)));
       lds_u8* grp_s = grp + 64 * 128;
+      // (both waves of a group are active or neither: they share wm)
 #pragma unroll
       for (int fm = 0; fm < 2; ++fm) {
+        if (!active) break;
         const int t = 32 * fm + li;   // token row within the 64-token block
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
@@ -693,6 +712,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       }
       barrier();
       // wave wn stores rows [32 wn, 32 wn + 32) of its group: 8 lanes per row
+      if (active) {
       const int64_t hc0 = (int64_t)cur.nt * (BN / 2);
       u32x4 v[4];
 #pragma unroll
@@ -709,6 +729,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       }
       if (lg == 0 && 64 * wm + 32 * wn + li < cur.rows_valid)
         *reinterpret_cast<uint32_t*>(p.hs + (cur.m0 + 64 * wm + 32 * wn + li) * (I / 32) + hc0 / 32) = sw_word;
+      }   // active
     }
     // every wave is done with the staging slot: issue the DMA the last stage
     // skipped, global stage g + 1 (the next tile's stage 1, or with one stage
