@@ -272,8 +272,8 @@ size_t mx_linear_workspace_size(int64_t T, int64_t K);
  *   (xq, xs) = MX quantisation of x along K (as mx_quantize)
  *   y[t, n]  = bf16_rne( sum over 32-blocks b of 2^(sx[t,b] + sw[n,b]) * (xq[t,b] . wq[n,b]) )
  *   x bf16 [T, K]; w uint8 [N, K] e4m3; w_s uint8 [N, K/64, 2]; y bf16 [T, N].
- * The workspace (mx_linear_workspace_size, 256-byte aligned) holds xq, xs
- * and a one-entry group list.  Limits as gmm_mx with one group: K % 128 == 0,
+ * The workspace (mx_linear_workspace_size, 256-byte aligned) holds xq and
+ * xs.  Limits as gmm_mx with one group: K % 128 == 0,
  * N % 256 == 0.
  */
 int mx_linear(const void* x_bf16, const void* w_u8, const void* w_s,

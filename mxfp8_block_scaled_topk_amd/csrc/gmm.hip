@@ -114,7 +114,12 @@ struct Stage {
   uint32_t sb[BM];
 };
 
-__device__ __forceinline__ int64_t group_count(const int64_t* gl, int type, int e) {
+// Group-list types: 0 cumulative, 1 counts (the entry points' two forms);
+// 2, used only inside the library (the dense linear), one group holding all
+// M rows with no list in memory.
+constexpr int kGlSingle = 2;
+__device__ __forceinline__ int64_t group_count(const int64_t* gl, int type, int e, int64_t M) {
+  if (type == kGlSingle) return e == 0 ? M : 0;
   if (type == 1) return gl[e];
   return gl[e] - (e > 0 ? gl[e - 1] : 0);
 }
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = lane * PER + i;
-      int64_t v = e < E ? group_count(p.group_list, p.gl_type, e) : 0;
+      int64_t v = e < E ? group_count(p.group_list, p.gl_type, e, p.M) : 0;
       v = v < 0 ? 0 : (v > p.M ? p.M : v);
       n[i] = v;
       local += v;

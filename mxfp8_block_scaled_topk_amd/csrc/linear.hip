@@ -7,8 +7,7 @@
 //   y [T, N] = bf16( sum over blocks 2^(sx + sw) * (xq . wq) )   (gmm_mx, one group)
 //
 // The GEMM is the grouped block-scaled MFMA GEMM with a single group of T
-// rows; its one-entry group list lives in the workspace and is written by a
-// one-thread kernel (not a memset, so the call stays capturable).
+// rows (group-list type 2 inside the library: no list in memory).
 #include "common.h"
 
 namespace mxmoe {
@@ -22,17 +21,14 @@ int launch_gmm_mx(const uint8_t* a, const uint8_t* as, const uint8_t* w, const u
 
 namespace {
 
-__global__ void set_single_group(int64_t* gl, int64_t rows) { gl[0] = rows; }
-
 struct LinearLayout {
-  size_t xq, xs, gl, total;
+  size_t xq, xs, total;
 };
 LinearLayout linear_layout(int64_t T, int64_t K) {
   LinearLayout L;
   L.xq = 0;
   L.xs = align_up((size_t)(T * K), 256);
-  L.gl = L.xs + align_up((size_t)(T * (K / 32)), 256);
-  L.total = L.gl + 256;
+  L.total = L.xs + align_up((size_t)(T * (K / 32)), 256);
   return L;
 }
 
@@ -66,12 +62,8 @@ extern "C" int mx_linear(const void* x_bf16, const void* w_u8, const void* w_s, 
   char* base = static_cast<char*>(workspace);
   uint8_t* xq = reinterpret_cast<uint8_t*>(base + L.xq);
   uint8_t* xs = reinterpret_cast<uint8_t*>(base + L.xs);
-  int64_t* gl = reinterpret_cast<int64_t*>(base + L.gl);
-  set_single_group<<<dim3(1), dim3(1), 0, s>>>(gl, T);
-  rc = check_launch("mx_linear(group list)");
-  if (rc) return rc;
   rc = launch_mx_quantize(static_cast<const uint16_t*>(x_bf16), T, K, K, xq, xs, s);
   if (rc) return rc;
-  return launch_gmm_mx(xq, xs, static_cast<const uint8_t*>(w_u8), static_cast<const uint8_t*>(w_s), gl, 1, T, N, K,
-                       1, static_cast<uint16_t*>(y_bf16), s, false);
+  return launch_gmm_mx(xq, xs, static_cast<const uint8_t*>(w_u8), static_cast<const uint8_t*>(w_s), nullptr,
+                       /*single group of T rows*/ 2, T, N, K, 1, static_cast<uint16_t*>(y_bf16), s, false);
 }
