@@ -105,8 +105,8 @@ def main():
                          "calibrates the FETCH_SIZE / WRITE_SIZE hardware counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (one GPU holds all experts); "
-              "--gpus must be 1", file=sys.stderr)
+        print("bench.py: the layer is measured on one GPU only (one GPU holds all experts; "
+              "expert-parallel sharding is not implemented); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
     cfg = CFG
