@@ -208,6 +208,10 @@ GMM_CASES = {
     "tiny-rows": ([1, 1, 1, 2], 128, 512),
     "wide-k": ([64, 200, 33], 1024, 256),
     "multi-tile-n": ([700, 20], 256, 768),
+    # tail tiles whose valid rows end at or just past a wave's 32- or
+    # 64-token boundary (waves skip MFMAs / token DMA); K = 512 runs the
+    # 4-stage scale groups
+    "tail-boundaries": ([64, 65, 192, 193, 32, 33, 128, 1], 512, 256),
 }
 
 
@@ -290,6 +294,7 @@ GMM1_CASES = {
     "ragged": ([3, 0, 128, 129, 1, 260, 256, 511], 256, 128),
     "wide-i": ([70, 150], 128, 384),
     "single": ([1], 512, 128),
+    "tail-boundaries": ([64, 65, 192, 193, 32, 33, 1], 512, 128),
 }
 
 
@@ -319,6 +324,41 @@ def test_gmm_swiglu_mxquant_parity(name):
     hq0, hs0 = mx.gmm_swiglu_mxquant(u8_dev(aq), u8_dev(as_), u8_dev(wq), u8_dev(ws), i64_dev(np.cumsum(counts)), 0)
     torch.cuda.synchronize()
     assert np.array_equal(host(hq0), host(hq)) and np.array_equal(host(hs0), host(hs))
+
+
+def _offset_u8_dev(a, offset=4):
+    """uint8 device copy whose data pointer is 4 bytes past a 256-byte
+    aligned allocation: 4-byte aligned, not 16-byte aligned."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    buf = torch.zeros(a.size + 64, dtype=torch.uint8, device="cuda")
+    v = buf[offset:offset + a.size]
+    v.copy_(torch.from_numpy(a.reshape(-1)).to("cuda"))
+    assert v.data_ptr() % 16 == offset
+    return v.view(a.shape)
+
+
+def test_gmm_scales_not_16_byte_aligned():
+    """Scale tensors that are 4- but not 16-byte aligned take the per-stage
+    scale loads even where the k stages divide into groups of 4; both GEMMs
+    still match the oracle."""
+    counts = np.array([100, 0, 300, 45], np.int64)
+    M, E, K, I, N = int(counts.sum()), len(counts), 512, 128, 256
+    say(f"gemms with 4-byte-aligned scales M={M} K={K}")
+    aq, as_, wq, ws = _mx_operands(M, K, E, N)
+    y = mx.gmm_mx(u8_dev(aq), _offset_u8_dev(as_), u8_dev(wq), _offset_u8_dev(ws), i64_dev(counts), 1)
+    torch.cuda.synchronize()
+    err = bf16_rows_rel_err(bf16_host(y), moe_ref.gmm_mx_ref(aq, as_, wq, ws, counts, 1))
+    say(f"  gmm_mx max row rel err {err.max():.3g}")
+    assert err.max() <= TOL
+    aq, as_, wq, ws = _mx_operands(M, K, E, 2 * I)
+    hq, hs, h = mx.gmm_swiglu_mxquant(u8_dev(aq), _offset_u8_dev(as_), u8_dev(wq), _offset_u8_dev(ws),
+                                      i64_dev(counts), 1, h_debug=True)
+    torch.cuda.synchronize()
+    rq, rs, rh = moe_ref.gmm_swiglu_mxquant_ref(aq, as_, wq, ws, counts, 1, I)
+    hk = host(h)
+    assert row_rel_err(hk, rh).max() <= 1e-3
+    kq, ks = mx_ref.mx_quantize_ref(hk.astype(np.float64))
+    assert np.array_equal(host(hq), kq) and np.array_equal(host(hs), ks)
 
 
 def test_gmm_swiglu_gate_up_closed_form():
