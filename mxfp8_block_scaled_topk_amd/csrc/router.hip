@@ -13,13 +13,15 @@
 // k-values [8 (l/32), 8 (l/32) + 8) of the 16-wide step; output lane l holds
 // column l % 32 and rows 8 q + 4 (l/32) + (0..3) in accumulator elements
 // 4 q .. 4 q + 3).  Gate rows are the A operand (experts), token rows the B
-// operand.  K advances 64 values (128 bytes per row) per chunk through a
-// double-buffered LDS tile of the 64 token rows and the E gate rows, loaded
-// with 16-byte coalesced loads that run four chunks ahead through a ring of
-// register sets (measured: with one chunk ahead the kernel waited out a
-// memory round trip per chunk); 16-byte chunk c of row r sits at chunk
-// c ^ (r % 8), which keeps the fragment reads (32 rows, one chunk) spread
-// over the LDS banks.  Wave w covers tokens 32 (w % 2) .. + 32 and expert
+// operand.  K advances 64 values (128 bytes per row) per chunk through a ring
+// of S LDS slots, each holding the 64 token rows and the E gate rows of one
+// chunk, filled by direct global->LDS loads (1 KB = 8 rows per instruction,
+// no staging registers) running S-1 chunks ahead: the kernel is bound by
+// how many bytes are in flight per CU (measured: a 4-deep ring of register
+// sets, about 72 KB in flight, ran 0.78 us per chunk).  16-byte chunk c of
+// row r sits at chunk c ^ (r % 8), which keeps the fragment reads (32 rows,
+// one chunk) spread over the LDS banks; the swizzle is applied on the global
+// side by choosing which chunk each DMA lane fetches.  Wave w covers tokens 32 (w % 2) .. + 32 and expert
 // tiles w / 2, w / 2 + 2, ...  The logits then go through LDS to a quad of
 // 4 lanes per token for the softmax and the selection (measured: one thread
 // per token walking its row in LDS took two thirds of the kernel's time).  HBM-bound: x is read once
@@ -40,10 +42,24 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-struct Buf {
-  uint8_t x[kBT * kRow];     // 8 KB
-  uint8_t g[kMaxE * kRow];   // 32 KB
+// LDS ring: slots of 64 token rows then Ep gate rows, 128 bytes each; Ep <=
+// 64 NT rows.  Slots per ring: as many as fit in 160 KB, at most 6.
+template <int NT>
+struct Ring {
+  static constexpr int kSlotBytes = (kBT + 64 * NT) * kRow;
+  static constexpr int kSlots = (160 * 1024) / kSlotBytes < 6 ? (160 * 1024) / kSlotBytes : 6;
 };
+
+// 64 lanes x 16 B from global (uniform base + per-lane 32-bit offset) to LDS
+// [m0, m0 + 1024).
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // byte offset of 16-byte chunk c of row r in a tile of 128-byte rows
 __device__ __forceinline__ int swz(int r, int c) { return r * kRow + ((c ^ (r & 7)) << 4); }
@@ -71,27 +87,6 @@ __device__ __forceinline__ float quad_sum(float x) {
   x += quad_swapf1(x);
   return x + quad_swapf2(x);
 }
-// (bv, be) <- the quad's largest bv, the lowest be among equal ones; lanes
-// with be == kNone hold no candidate.
-__device__ __forceinline__ void quad_argmax(float& bv, int& be) {
-  auto take = [&](float ov, int oe) {
-    if (oe != kNone && (be == kNone || ov > bv || (ov == bv && oe < be))) {
-      bv = ov;
-      be = oe;
-    }
-  };
-  {
-    const float ov = quad_swapf1(bv);
-    const int oe = quad_swap<kQuadXor1>(be);
-    take(ov, oe);
-  }
-  {
-    const float ov = quad_swapf2(bv);
-    const int oe = quad_swap<kQuadXor2>(be);
-    take(ov, oe);
-  }
-}
-
 template <int NT>   // expert tiles per wave (ceil(E/32) / 2, rounded up)
 __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ gate,
@@ -99,49 +94,45 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
                                                           int E, int k, int renormalize,
                                                           int32_t* __restrict__ topk_ids,
                                                           float* __restrict__ topk_w) {
-  __shared__ __attribute__((aligned(16))) Buf buf[2];
+  constexpr int kS = Ring<NT>::kSlots;
+  constexpr int kSlotBytes = Ring<NT>::kSlotBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kS * kSlotBytes];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t t0 = (int64_t)blockIdx.x * kBT;
   const int Ep = (E + 31) & ~31;   // expert rows held in LDS
   const int nchunks = (int)(K / kCK);
 
-  // ---- global -> registers -> LDS, one chunk ---------------------------------
-  // x: 64 rows x 8 chunks, 2 per thread; gate: 64 NT rows (>= Ep) x 8 chunks,
-  // 2 NT per thread.  Rows past T or E repeat the last row (their logits are
-  // never selected or stored), so every thread issues the same loads.
-  constexpr int kGPer = 2 * NT * 32 * 8 / kThreads;
-  struct Regs {
-    u32x4 x[2], g[kGPer];
-  };
-  auto load = [&](Regs& R, int ch) __attribute__((always_inline)) {
-    u32x4(&rx)[2] = R.x;
-    u32x4(&rg)[kGPer] = R.g;
+  // ---- the DMA of one chunk --------------------------------------------------------
+  // Instruction i fills LDS rows [8 i, 8 i + 8) of the slot: i < 8 token rows,
+  // then 8 NT instructions of gate rows (64 NT rows, the tier's maximum, so
+  // every wave issues the same kOps per chunk whatever E is); wave w issues
+  // i = w, w + 4, ...  Lane l lands at row 8 i + l/8, physical chunk l%8, and
+  // fetches logical chunk (l%8) ^ ((l/8)%8).  Rows past T or E repeat the last
+  // row (their logits are never selected or stored).
+  constexpr int kOps = (8 + 8 * NT) / 4;   // per wave per chunk
+  const int lrow = lane >> 3, lchk = (lane & 7) ^ (lrow & 7);
+  const uint32_t ring_base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)ring;
+  const int tlast = (int)(T - 1 - t0 < kBT - 1 ? T - 1 - t0 : kBT - 1);   // last readable token row
+  const uint16_t* xrow = x + t0 * K;
+  auto dma_chunk = [&](int ch, int slot) __attribute__((always_inline)) {
+    const uint32_t sbase = ring_base + (uint32_t)(slot * kSlotBytes);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int piece = tid + i * kThreads, r = piece >> 3, c = piece & 7;
-      const int64_t row = t0 + r < T ? t0 + r : T - 1;
-      rx[i] = *reinterpret_cast<const u32x4*>(x + row * K + (int64_t)ch * kCK + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < kGPer; ++i) {
-      const int piece = tid + i * kThreads, r = piece >> 3, c = piece & 7;
-      const int row = r < E ? r : E - 1;
-      rg[i] = *reinterpret_cast<const u32x4*>(gate + (int64_t)row * K + (int64_t)ch * kCK + c * 8);
-    }
-  };
-  auto store = [&](const Regs& R, Buf& b) __attribute__((always_inline)) {
-    const u32x4(&rx)[2] = R.x;
-    const u32x4(&rg)[kGPer] = R.g;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int piece = tid + i * kThreads, r = piece >> 3, c = piece & 7;
-      *reinterpret_cast<u32x4*>(b.x + swz(r, c)) = rx[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kGPer; ++i) {
-      const int piece = tid + i * kThreads, r = piece >> 3, c = piece & 7;
-      *reinterpret_cast<u32x4*>(b.g + swz(r, c)) = rg[i];
+    for (int j = 0; j < kOps; ++j) {
+      const int i = wave + 4 * j;
+      int r = 8 * i + lrow;   // LDS row in the slot
+      const void* base;
+      uint32_t voff;
+      if (i < 8) {
+        const int tr = r < tlast ? r : tlast;
+        base = xrow;
+        voff = (uint32_t)(tr * K * 2 + ch * kRow + lchk * 16);
+      } else {
+        const int er = r - kBT < E - 1 ? r - kBT : E - 1;
+        base = gate;
+        voff = (uint32_t)(er * K * 2 + ch * kRow + lchk * 16);
+      }
+      dma16(voff, base, sbase + (uint32_t)(8 * i * kRow));
     }
   };
 
@@ -153,49 +144,50 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
 
-  // A ring of kDepth register sets: while chunk ch is multiplied, chunks
-  // ch+1 .. ch+kDepth-1 are in flight or waiting in registers, and chunk
-  // ch+kDepth is requested (one memory round trip per ~3 chunks of work).
-  auto mfma_chunk = [&](const Buf& b) __attribute__((always_inline)) {
+  // All of a chunk's fragment reads go out before its MFMAs, so their LDS
+  // latencies overlap (one wave per SIMD: nothing else hides them).
+  auto mfma_chunk = [&](int slot) __attribute__((always_inline)) {
+    const uint8_t* bx = ring + slot * kSlotBytes;
+    const uint8_t* bg = bx + kBT * kRow;
+    bf16x8 xb[kCK / 16], gb[kCK / 16][NT];
 #pragma unroll
     for (int s = 0; s < kCK / 16; ++s) {
       const int c = 2 * s + lg;   // this lane's 16-byte chunk of the step
-      const bf16x8 xb = *reinterpret_cast<const bf16x8*>(b.x + swz(32 * th + li, c));
+      xb[s] = *reinterpret_cast<const bf16x8*>(bx + swz(32 * th + li, c));
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         const int et = eh + 2 * i;
-        if (32 * et < Ep) {
-          const bf16x8 gb = *reinterpret_cast<const bf16x8*>(b.g + swz(32 * et + li, c));
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gb, xb, acc[i], 0, 0, 0);
-        }
+        const int er = 32 * et < Ep ? 32 * et + li : li;   // absent tiles read a valid row, unused
+        gb[s][i] = *reinterpret_cast<const bf16x8*>(bg + swz(er, c));
       }
     }
-  };
-  // one step: multiply chunk ch (in buf[ch&1]), load chunk ch+kDepth into
-  // `next` (it held chunk ch, already in LDS), move chunk ch+1 from `held`
-  // into the other buffer
-  constexpr int kDepth = 4;
-  auto step = [&](int ch, Regs& held, Regs& next) __attribute__((always_inline)) {
-    if (ch + kDepth < nchunks) load(next, ch + kDepth);
-    mfma_chunk(buf[ch & 1]);
-    if (ch + 1 < nchunks) store(held, buf[(ch + 1) & 1]);
-    __syncthreads();
-  };
-  Regs R[kDepth];
 #pragma unroll
-  for (int j = 0; j < kDepth; ++j)
-    if (j < nchunks) load(R[j], j);
-  store(R[0], buf[0]);
-  __syncthreads();
-  for (int ch = 0; ch < nchunks; ch += kDepth) {
-    step(ch, R[1], R[0]);
-    if (ch + 1 < nchunks) step(ch + 1, R[2], R[1]);
-    if (ch + 2 < nchunks) step(ch + 2, R[3], R[2]);
-    if (ch + 3 < nchunks) step(ch + 3, R[0], R[3]);
-  }
+    for (int s = 0; s < kCK / 16; ++s)
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+        if (32 * (eh + 2 * i) < Ep) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gb[s][i], xb[s], acc[i], 0, 0, 0);
+  };
 
-  // ---- logits to LDS: [64 tokens][Ep] fp32 (reuses both buffers) ----------------
-  float* L = reinterpret_cast<float*>(&buf[0]);
+  // prologue: chunks 0 .. kS-2 in flight; chunk ch lives in slot ch % kS
+  for (int c = 0; c < kS - 1; ++c)
+    if (c < nchunks) dma_chunk(c, c);
+  for (int ch = 0; ch < nchunks; ++ch) {
+    // this wave's part of chunk ch has landed once at most the kS-2 later
+    // chunks' loads are outstanding (loads retire in order; near the end,
+    // with fewer later chunks issued, wait for all); the barrier makes every
+    // wave's part visible and frees the slot of chunk ch - 1
+    if (ch + kS - 2 < nchunks)
+      wait_vmcnt<(kS - 2) * kOps>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    if (ch + kS - 1 < nchunks) dma_chunk(ch + kS - 1, (ch + kS - 1) % kS);
+    mfma_chunk(ch % kS);
+  }
+  __syncthreads();
+
+  // ---- logits to LDS: [64 tokens][Ep] fp32 (reuses the ring) ---------------------
+  float* L = reinterpret_cast<float*>(ring);
   const int ldl = Ep + 1;   // padded row: the 32 lanes of a store hit distinct banks
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
@@ -227,25 +219,38 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
       lm = fmaxf(lm, v[i]);               // fmaxf ignores the NaN
     }
     const float m = quad_max(lm);
-    float ls = 0.0f;
+    // four partial sums: independent chains (one wave per SIMD hides no latency)
+    float ls4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < NPER; ++i)
-      if (v[i] == v[i]) ls += expf(v[i] - m);
-    const float sum = quad_sum(ls);
+      if (v[i] == v[i]) ls4[i & 3] += expf(v[i] - m);
+    const float sum = quad_sum((ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
     const int64_t o = (t0 + t) * k;
     float wsel = 0.0f;
     for (int j = 0; j < k; ++j) {
-      // this lane's best: the largest logit, the lower id on ties (ascending
-      // i is ascending id); be = kNone when the lane has nothing left
-      float bv = -INFINITY;
-      int be = kNone;
+      // the token's best: the largest remaining logit (a max tree over the
+      // lane's values, fmaxf ignoring the NaN of taken experts, then over the
+      // quad), and among equal ones the lowest id (a min tree over the ids
+      // holding that value); trees instead of one running comparison keep the
+      // dependency chains short
+      float t[NPER];
 #pragma unroll
-      for (int i = 0; i < NPER; ++i)
-        if (v[i] == v[i] && (be == kNone || v[i] > bv)) {
-          bv = v[i];
-          be = 4 * i + q;
-        }
-      quad_argmax(bv, be);
+      for (int i = 0; i < NPER; ++i) t[i] = v[i];
+#pragma unroll
+      for (int w = NPER / 2; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
+      const float bv = quad_max(t[0]);
+      int c[NPER];
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) c[i] = v[i] == bv ? 4 * i + q : kNone;
+#pragma unroll
+      for (int w = NPER / 2; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) c[i] = c[i] < c[i + w] ? c[i] : c[i + w];
+      int be = c[0];
+      be = min(be, quad_swap<kQuadXor1>(be));
+      be = min(be, quad_swap<kQuadXor2>(be));
 #pragma unroll
       for (int i = 0; i < NPER; ++i)
         if (4 * i + q == be) v[i] = NAN;
