@@ -181,8 +181,10 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
     else
       wait_vmcnt<0>();
     __syncthreads();
-    if (ch + kS - 1 < nchunks) dma_chunk(ch + kS - 1, (ch + kS - 1) % kS);
+    // the MFMAs first: a DMA issue can stall the wave while the memory
+    // pipeline is full, and the matrix work should not wait behind it
     mfma_chunk(ch % kS);
+    if (ch + kS - 1 < nchunks) dma_chunk(ch + kS - 1, (ch + kS - 1) % kS);
   }
   __syncthreads();
 
