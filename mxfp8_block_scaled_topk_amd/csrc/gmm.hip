@@ -105,7 +105,6 @@ struct GmmParams {
 
 constexpr int SK = 128;          // K bytes per stage (whole 128-byte rows)
 constexpr int kSlots = 2;        // LDS ring slots
-constexpr int kDmaPerStage = 9;  // per wave: 4 (A) + 4 (B) x 1 KB, 1 scale load
 
 struct Stage {
   uint8_t a[BN * SK];
