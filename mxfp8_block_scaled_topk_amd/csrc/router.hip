@@ -8,31 +8,32 @@
 //   ids = the k largest logits, descending (equal logits: lower id first)
 //   w[j] = p[ids[j]], divided by the sum of the k when renormalising
 //
-// One workgroup of 4 waves handles 64 tokens.  The gate GEMM runs on the bf16
-// MFMA (V_MFMA_F32_32X32X16_BF16: lane l holds operand row l % 32 and the 8
-// k-values [8 (l/32), 8 (l/32) + 8) of the 16-wide step; output lane l holds
-// column l % 32 and rows 8 q + 4 (l/32) + (0..3) in accumulator elements
-// 4 q .. 4 q + 3).  Gate rows are the A operand (experts), token rows the B
-// operand.  K advances 64 values (128 bytes per row) per chunk through a ring
-// of S LDS slots, each holding the 64 token rows and the E gate rows of one
-// chunk, filled by direct global->LDS loads (1 KB = 8 rows per instruction,
-// no staging registers) running S-1 chunks ahead: the kernel is bound by
-// how many bytes are in flight per CU (measured: a 4-deep ring of register
-// sets, about 72 KB in flight, ran 0.78 us per chunk).  16-byte chunk c of
-// row r sits at chunk c ^ (r % 8), which keeps the fragment reads (32 rows,
-// one chunk) spread over the LDS banks; the swizzle is applied on the global
-// side by choosing which chunk each DMA lane fetches.  Wave w covers tokens 32 (w % 2) .. + 32 and expert
-// tiles w / 2, w / 2 + 2, ...  The logits then go through LDS to a quad of
-// 4 lanes per token for the softmax and the selection (measured: one thread
-// per token walking its row in LDS took two thirds of the kernel's time).  HBM-bound: x is read once
-// (2 T K bytes), the gate comes from L2.
+// One workgroup of 8 waves (two per SIMD) handles 64 tokens.  The gate GEMM
+// runs on the bf16 MFMA (V_MFMA_F32_32X32X16_BF16: lane l holds operand row
+// l % 32 and the 8 k-values [8 (l/32), 8 (l/32) + 8) of the 16-wide step;
+// output lane l holds column l % 32 and rows 8 q + 4 (l/32) + (0..3) in
+// accumulator elements 4 q .. 4 q + 3).  Gate rows are the A operand
+// (experts), token rows the B operand.  K advances 64 values (128 bytes per
+// row) per chunk through a ring of S LDS slots, each holding the 64 token rows
+// and the gate rows of one chunk, filled by direct global->LDS loads (1 KB =
+// 8 rows per instruction, no staging registers) running S-1 chunks ahead
+// (measured: a 4-deep ring of register sets, about 72 KB in flight per CU,
+// ran 0.78 us per chunk).  16-byte chunk c of row r sits at chunk c ^ (r % 8),
+// which keeps the fragment reads (32 rows, one chunk) spread over the LDS
+// banks; the swizzle is applied on the global side by choosing which chunk
+// each DMA lane fetches.  Wave w covers tokens 32 (w % 2) .. + 32 and expert
+// tiles w / 2, w / 2 + 4, ...  The logits then go through LDS to 8 lanes per
+// token for the softmax and the selection (measured: one thread per token
+// walking its row in LDS took two thirds of the kernel's time; with one wave
+// per SIMD the selection's dependency chains were latency-bound).  HBM-bound:
+// x is read once (2 T K bytes), the gate comes from L2.
 #include "common.h"
 
 namespace mxmoe {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;   // 8 waves, two per SIMD
 constexpr int kBT = 64;        // tokens per workgroup
 constexpr int kCK = 64;        // k values per chunk (128 bytes of a row)
 constexpr int kMaxE = 256;
@@ -79,15 +80,27 @@ __device__ __forceinline__ float quad_swapf1(float x) {
 __device__ __forceinline__ float quad_swapf2(float x) {
   return __int_as_float(quad_swap<kQuadXor2>(__float_as_int(x)));
 }
-__device__ __forceinline__ float quad_max(float x) {
+// Exchange with the lane whose index differs in bit 2 (ds_swizzle, xor mask 4
+// within each 32-lane half).
+__device__ __forceinline__ int swap4(int x) { return __builtin_amdgcn_ds_swizzle(x, 0x101f); }
+__device__ __forceinline__ float swapf4(float x) { return __int_as_float(swap4(__float_as_int(x))); }
+// Reductions over the 8 lanes (an aligned group) that hold one token.
+__device__ __forceinline__ float oct_max(float x) {
   x = fmaxf(x, quad_swapf1(x));
-  return fmaxf(x, quad_swapf2(x));
+  x = fmaxf(x, quad_swapf2(x));
+  return fmaxf(x, swapf4(x));
 }
-__device__ __forceinline__ float quad_sum(float x) {
+__device__ __forceinline__ float oct_sum(float x) {
   x += quad_swapf1(x);
-  return x + quad_swapf2(x);
+  x += quad_swapf2(x);
+  return x + swapf4(x);
 }
-template <int NT>   // expert tiles per wave (ceil(E/32) / 2, rounded up)
+__device__ __forceinline__ int oct_min(int x) {
+  x = min(x, quad_swap<kQuadXor1>(x));
+  x = min(x, quad_swap<kQuadXor2>(x));
+  return min(x, swap4(x));
+}
+template <int NT>   // gate rows held per chunk: 64 NT (E <= 64 NT)
 __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ gate,
                                                           const float* __restrict__ bias, int64_t T, int64_t K,
@@ -107,10 +120,10 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
   // Instruction i fills LDS rows [8 i, 8 i + 8) of the slot: i < 8 token rows,
   // then 8 NT instructions of gate rows (64 NT rows, the tier's maximum, so
   // every wave issues the same kOps per chunk whatever E is); wave w issues
-  // i = w, w + 4, ...  Lane l lands at row 8 i + l/8, physical chunk l%8, and
+  // i = w, w + 8, ...  Lane l lands at row 8 i + l/8, physical chunk l%8, and
   // fetches logical chunk (l%8) ^ ((l/8)%8).  Rows past T or E repeat the last
   // row (their logits are never selected or stored).
-  constexpr int kOps = (8 + 8 * NT) / 4;   // per wave per chunk
+  constexpr int kOps = (8 + 8 * NT) / 8;   // per wave per chunk
   const int lrow = lane >> 3, lchk = (lane & 7) ^ (lrow & 7);
   const uint32_t ring_base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)ring;
   const int tlast = (int)(T - 1 - t0 < kBT - 1 ? T - 1 - t0 : kBT - 1);   // last readable token row
@@ -119,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
     const uint32_t sbase = ring_base + (uint32_t)(slot * kSlotBytes);
 #pragma unroll
     for (int j = 0; j < kOps; ++j) {
-      const int i = wave + 4 * j;
+      const int i = wave + 8 * j;
       int r = 8 * i + lrow;   // LDS row in the slot
       const void* base;
       uint32_t voff;
@@ -136,11 +149,13 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
     }
   };
 
+  // wave w: tokens 32 (w % 2) .. + 32, expert tiles w/2, w/2 + 4, ...
+  constexpr int NTW = NT > 1 ? NT / 2 : 1;   // expert tiles per wave
   const int th = wave & 1, eh = wave >> 1;
   const int li = lane & 31, lg = lane >> 5;
-  v16f acc[NT];
+  v16f acc[NTW];
 #pragma unroll
-  for (int i = 0; i < NT; ++i)
+  for (int i = 0; i < NTW; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
 
@@ -149,14 +164,14 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
   auto mfma_chunk = [&](int slot) __attribute__((always_inline)) {
     const uint8_t* bx = ring + slot * kSlotBytes;
     const uint8_t* bg = bx + kBT * kRow;
-    bf16x8 xb[kCK / 16], gb[kCK / 16][NT];
+    bf16x8 xb[kCK / 16], gb[kCK / 16][NTW];
 #pragma unroll
     for (int s = 0; s < kCK / 16; ++s) {
       const int c = 2 * s + lg;   // this lane's 16-byte chunk of the step
       xb[s] = *reinterpret_cast<const bf16x8*>(bx + swz(32 * th + li, c));
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        const int et = eh + 2 * i;
+      for (int i = 0; i < NTW; ++i) {
+        const int et = eh + 4 * i;
         const int er = 32 * et < Ep ? 32 * et + li : li;   // absent tiles read a valid row, unused
         gb[s][i] = *reinterpret_cast<const bf16x8*>(bg + swz(er, c));
       }
@@ -164,8 +179,8 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
 #pragma unroll
     for (int s = 0; s < kCK / 16; ++s)
 #pragma unroll
-      for (int i = 0; i < NT; ++i)
-        if (32 * (eh + 2 * i) < Ep) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gb[s][i], xb[s], acc[i], 0, 0, 0);
+      for (int i = 0; i < NTW; ++i)
+        if (32 * (eh + 4 * i) < Ep) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gb[s][i], xb[s], acc[i], 0, 0, 0);
   };
 
   // prologue: chunks 0 .. kS-2 in flight; chunk ch lives in slot ch % kS
@@ -192,8 +207,8 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
   float* L = reinterpret_cast<float*>(ring);
   const int ldl = Ep + 1;   // padded row: the 32 lanes of a store hit distinct banks
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int et = eh + 2 * i;
+  for (int i = 0; i < NTW; ++i) {
+    const int et = eh + 4 * i;
     if (32 * et < Ep) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -204,35 +219,35 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
   __syncthreads();
 
   // ---- per token: softmax, top-k, weights --------------------------------------
-  // A quad of 4 lanes per token (the 256 threads cover the 64 tokens): lane q
-  // holds the logits of experts 4 i + q in registers, reductions across the
-  // quad use DPP quad permutes.  A taken (or absent) expert is NaN.
+  // 8 lanes per token (the 512 threads cover the 64 tokens): lane q holds the
+  // logits of experts 8 i + q in registers; reductions across the 8 use DPP
+  // quad permutes and one swizzle.  A taken (or absent) expert is NaN.
   {
-    constexpr int NPER = 16 * NT;          // experts per lane (E <= 64 NT)
-    const int t = tid >> 2, q = tid & 3;
+    constexpr int NPER = 8 * NT;           // experts per lane (E <= 64 NT)
+    const int t = tid >> 3, q = tid & 7;
     const bool live = t0 + t < T;
     float* lt = L + t * ldl;
     float v[NPER];
     float lm = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
-      const int e = 4 * i + q;
+      const int e = 8 * i + q;
       v[i] = e < E ? lt[e] + (bias ? bias[e] : 0.0f) : NAN;
       lm = fmaxf(lm, v[i]);               // fmaxf ignores the NaN
     }
-    const float m = quad_max(lm);
-    // four partial sums: independent chains (one wave per SIMD hides no latency)
+    const float m = oct_max(lm);
+    // four partial sums: independent chains
     float ls4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < NPER; ++i)
       if (v[i] == v[i]) ls4[i & 3] += expf(v[i] - m);
-    const float sum = quad_sum((ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
+    const float sum = oct_sum((ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
     const int64_t o = (t0 + t) * k;
     float wsel = 0.0f;
     for (int j = 0; j < k; ++j) {
       // the token's best: the largest remaining logit (a max tree over the
       // lane's values, fmaxf ignoring the NaN of taken experts, then over the
-      // quad), and among equal ones the lowest id (a min tree over the ids
+      // token's 8 lanes), and among equal ones the lowest id (a min tree over the ids
       // holding that value); trees instead of one running comparison keep the
       // dependency chains short
       float t[NPER];
@@ -242,20 +257,18 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
       for (int w = NPER / 2; w >= 1; w >>= 1)
 #pragma unroll
         for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
-      const float bv = quad_max(t[0]);
+      const float bv = oct_max(t[0]);
       int c[NPER];
 #pragma unroll
-      for (int i = 0; i < NPER; ++i) c[i] = v[i] == bv ? 4 * i + q : kNone;
+      for (int i = 0; i < NPER; ++i) c[i] = v[i] == bv ? 8 * i + q : kNone;
 #pragma unroll
       for (int w = NPER / 2; w >= 1; w >>= 1)
 #pragma unroll
         for (int i = 0; i < w; ++i) c[i] = c[i] < c[i + w] ? c[i] : c[i + w];
-      int be = c[0];
-      be = min(be, quad_swap<kQuadXor1>(be));
-      be = min(be, quad_swap<kQuadXor2>(be));
+      const int be = oct_min(c[0]);
 #pragma unroll
       for (int i = 0; i < NPER; ++i)
-        if (4 * i + q == be) v[i] = NAN;
+        if (8 * i + q == be) v[i] = NAN;
       const float pe = expf(bv - m);
       wsel += pe;
       if (q == 0) lt[j] = pe;             // the row's logits are in registers now
@@ -263,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
     }
     const float den = renormalize ? wsel : sum;
     if (live)
-      for (int j = q; j < k; j += 4) topk_w[o + j] = lt[j] / den;
+      for (int j = q; j < k; j += 8) topk_w[o + j] = lt[j] / den;
   }
 }
 
