@@ -24,6 +24,11 @@
 //                        prefill size).  The kernel is bound by HBM writes
 //                        (k quantised copies of every token).
 //
+// When all T*k assignments fit in one chunk (decode-sized batches) the
+// histogram and scan launches are skipped: the scatter blocks take the
+// experts' totals from their own per-wave counts (prefix 0 for the only
+// chunk), and the first block writes the group list.
+//
 // The order inside an expert is the flat index order, so the permutation is
 // deterministic and equals a stable sort by expert.
 #include <algorithm>
@@ -95,7 +100,9 @@ __global__ __launch_bounds__(kThreads) void route_scan(int32_t* __restrict__ cou
 }
 
 // Exclusive scan of v[0..n) (n <= 1024) into out[0..n) by one 256-thread block.
-__device__ void block_exclusive_scan(const int32_t* __restrict__ v, int n, int* out, int* s_wsum) {
+// Every read of v precedes the block barrier inside and every write to out
+// follows it, so out may be v (in place).
+__device__ void block_exclusive_scan(const int32_t* v, int n, int* out, int* s_wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int loc[4];
   int sum = 0;
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter_quant(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, int64_t T, int64_t K, int k,
     int E, int nbits, int tpc, int nchunks, const int32_t* __restrict__ prefix,
     const int32_t* __restrict__ totals, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
-    int32_t* __restrict__ sorted_row, int32_t* __restrict__ eri) {
+    int32_t* __restrict__ sorted_row, int32_t* __restrict__ eri, int64_t* __restrict__ group_list) {
   __shared__ int s_off[kMaxE];
   __shared__ int s_wcnt[kThreads / 64][kMaxE];
   __shared__ int s_pos[kThreads];
@@ -138,7 +145,8 @@ __global__ __launch_bounds__(kThreads) void route_scatter_quant(
   const int c = blockIdx.x / kSplit, part = blockIdx.x % kSplit;
   for (int w = 0; w < kThreads / 64; ++w)
     for (int e = tid; e < E; e += kThreads) s_wcnt[w][e] = 0;
-  block_exclusive_scan(totals, E, s_off, s_wsum);
+  const bool single = nchunks == 1;   // no histogram / scan launches (see the header)
+  if (!single) block_exclusive_scan(totals, E, s_off, s_wsum);
   __syncthreads();
 
   // ---- stable rank of each assignment within the chunk -------------------
@@ -161,10 +169,22 @@ __global__ __launch_bounds__(kThreads) void route_scatter_quant(
   int rank = __popcll(same & ((1ull << lane) - 1ull));
   if (valid && rank == 0) s_wcnt[wave][e] = __popcll(same);
   __syncthreads();
+  if (single) {
+    // the only chunk's counts are the experts' totals
+    for (int ee = tid; ee < E; ee += kThreads) {
+      int n = 0;
+      for (int w = 0; w < kThreads / 64; ++w) n += s_wcnt[w][ee];
+      s_off[ee] = n;
+      if (part == 0) group_list[ee] = n;
+    }
+    __syncthreads();
+    block_exclusive_scan(s_off, E, s_off, s_wsum);
+    __syncthreads();
+  }
   int pos = -1;
   if (valid) {
     for (int w = 0; w < wave; ++w) rank += s_wcnt[w][e];
-    pos = s_off[e] + prefix[(int64_t)e * nchunks + c] + rank;
+    pos = s_off[e] + (single ? 0 : prefix[(int64_t)e * nchunks + c]) + rank;
     if (part == 0) sorted_row[pos] = (int32_t)a;
   }
   if (part == 0 && tid < na) eri[a] = pos;
@@ -257,6 +277,11 @@ int launch_route_quant(const uint16_t* x, const int32_t* ids, int64_t T, int64_t
   }
   int nbits = 0;
   while ((1ll << nbits) < E) ++nbits;
+  if (nch == 1) {
+    route_scatter_quant<<<dim3((unsigned)kSplit), dim3(kThreads), 0, stream>>>(
+        x, ids, T, K, (int)k, (int)E, nbits, (int)tpc, 1, nullptr, nullptr, xq, xs, sorted_row, eri, group_list);
+    return check_launch("route_scatter_quant");
+  }
   route_hist<<<dim3((unsigned)nch), dim3(kThreads), 0, stream>>>(ids, T * k, (int)k, (int)E, (int)tpc,
                                                                    (int)nch, counts);
   int rc = check_launch("route_hist");
@@ -266,7 +291,8 @@ int launch_route_quant(const uint16_t* x, const int32_t* ids, int64_t T, int64_t
   rc = check_launch("route_scan");
   if (rc) return rc;
   route_scatter_quant<<<dim3((unsigned)(nch * kSplit)), dim3(kThreads), 0, stream>>>(
-      x, ids, T, K, (int)k, (int)E, nbits, (int)tpc, (int)nch, counts, totals, xq, xs, sorted_row, eri);
+      x, ids, T, K, (int)k, (int)E, nbits, (int)tpc, (int)nch, counts, totals, xq, xs, sorted_row, eri,
+      group_list);
   return check_launch("route_scatter_quant");
 }
 

@@ -124,6 +124,12 @@ ROUTE_CASES = {
     "E1": (33, 64, 1, 1, None),
     "k-eq-E": (50, 64, 6, 6, None),
     "big-k": (70, 64, 32, 40, None),
+    # T*k <= 256 is one routing chunk (no histogram/scan launches): the
+    # boundary on both sides, and the largest expert count in one chunk
+    "one-chunk-full": (32, 256, 8, 128, None),
+    "two-chunks-min": (33, 256, 8, 128, None),
+    "one-chunk-E1024": (16, 64, 8, 1024, None),
+    "one-chunk-hot": (60, 128, 4, 9, "hot"),
 }
 
 
