@@ -8,7 +8,7 @@ before timing starts.  One step = one moe_mxfp8_forward call over the whole
 batch: routing + fused MX activation quant, GEMM1 + SwiGLU + requant, GEMM2,
 finalize.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 50] [--no-cpu-baseline] [--no-workloads]
 
 Prints one JSON line.  After the headline loop a second loop runs the same
 four kernels through their own entry points with HIP events between them (on
@@ -19,7 +19,11 @@ object is computed from those.  The top-k router upstream of the layer
 dense MXFP8 linear layer (mx_linear, T=16384, K=N=4096, offline-style
 pre-quantised weight): a second workload of the same MX GEMM, not part of
 the MoE step.  And so is the same 16K prefill layer with MXFP4 (e2m1) expert
-weights (moe_w4a8_forward), with its two GEMMs timed separately.
+weights (moe_w4a8_forward), with its two GEMMs timed separately.  Last, the
+"workloads" object times the layer on all five shapes (tiny, decode, mid,
+16K prefill, wide prefill): per-step median/p10/p90, tokens/s, per-kernel
+medians and the GEMMs' TFLOP/s, plus cold-cache steps for the two small
+shapes.
 """
 
 import argparse
@@ -94,12 +98,121 @@ def cpu_baseline(d, tokens=2048):
                       f"full oracle layer, {dt:.1f} s"}
 
 
+def _dev_inputs(d, dev):
+    """A workload's layer inputs on the GPU.  Online workloads have their bf16
+    weights quantised by the library's mx_quantize (load time, not timed);
+    the offline one ships e4m3 bytes and scales."""
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    x = bf16(d["x"])
+    ids = torch.from_numpy(d["topk_ids"]).to(dev)
+    w = torch.from_numpy(d["topk_w"]).to(dev)
+    if d["cfg"].offline:
+        wts = [torch.from_numpy(d[n]).to(dev) for n in ("w13q", "w13s", "w2q", "w2s")]
+    else:
+        w13q, w13s = mx.mx_quantize(bf16(d["w13"]))
+        w2q, w2s = mx.mx_quantize(bf16(d["w2"]))
+        wts = [w13q, w13s, w2q, w2s]
+    return (x, ids, w, *wts)
+
+
+def _pct(v):
+    return {"us_median": round(float(np.median(v)), 2), "us_p10": round(float(np.percentile(v, 10)), 2),
+            "us_p90": round(float(np.percentile(v, 90)), 2)}
+
+
+def workload_table(dev, stream, prefill_inputs):
+    """All five layer shapes on one GPU: per-step layer time (HIP events on the
+    launch stream; median, p10, p90), tokens/s from the median, per-kernel
+    medians through the kernels' own entry points, the two GEMMs' combined
+    TFLOP/s, and for the two small shapes the layer time with the 256 MB
+    last-level cache flushed before every step (a 512 MB buffer written
+    between steps)."""
+    table = {}
+    for name in ("tiny", "decode", "mid", "prefill", "wide"):
+        cfg = CONFIGS[name]
+        T, K, I, E, k = cfg.T, cfg.K, cfg.I, cfg.E, cfg.k
+        print(f"bench.py: workload {name} (T={T} K={K} I={I} E={E} top-{k})", file=sys.stderr, flush=True)
+        small = T * k <= 256
+        steps = 500 if small else 50
+        if name == "prefill":
+            x, ids, w, w13, w13s, w2, w2s = prefill_inputs
+        else:
+            x, ids, w, w13, w13s, w2, w2s = _dev_inputs(make_inputs(cfg), dev)
+        ws = mx.forward_workspace(T, K, I, E, k, dev)
+        out = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            mx.moe_mxfp8_forward(x, ids, w, w13, w13s, w2, w2s, out=out, workspace=ws)
+
+        for _ in range(10):
+            step()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        lay = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+        ent = {"T": T, "K": K, "I": I, "E": E, "top_k": k, "steps": steps, **_pct(lay)}
+        ent["tokens_per_s"] = round(T / (ent["us_median"] * 1e-6), 1)
+
+        inter = mx.forward_intermediates(ws, T, K, I, E, k)
+        counts = inter["group_list"].cpu().numpy()
+        rws = torch.empty(mx.route_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
+        route_out = (inter["xq"], inter["xs"], inter["sorted_row"], inter["expanded_row_idx"], inter["group_list"])
+        ke = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        for s_ in range(steps):
+            e = ke[s_]
+            e[0].record(stream)
+            mx.moe_route_quant(x, ids, E, out=route_out, workspace=rws)
+            e[1].record(stream)
+            mx.gmm_swiglu_mxquant(inter["xq"], inter["xs"], w13, w13s, inter["group_list"], 1,
+                                  out=(inter["hq"], inter["hs"]))
+            e[2].record(stream)
+            mx.gmm_mx(inter["hq"], inter["hs"], w2, w2s, inter["group_list"], 1, out=inter["y"])
+            e[3].record(stream)
+            mx.moe_finalize(inter["y"], w, inter["expanded_row_idx"], out=out)
+            e[4].record(stream)
+        torch.cuda.synchronize()
+        kus = {n: float(np.median([ke[s_][i].elapsed_time(ke[s_][i + 1]) * 1e3 for s_ in range(steps)]))
+               for i, n in enumerate(["route_quant", "gemm1_swiglu_requant", "gemm2", "finalize"])}
+        ent["kernels_us_median"] = {n: round(v, 2) for n, v in kus.items()}
+        alg = algorithmic(cfg, counts)
+        gf = alg["gemm1_swiglu_requant"]["flops"] + alg["gemm2"]["flops"]
+        gtf = gf / ((kus["gemm1_swiglu_requant"] + kus["gemm2"]) * 1e-6) / 1e12
+        ent["gemm_TFLOPs"] = round(gtf, 1)
+        ent["gemm_mfma_frac"] = round(gtf / MFMA_FP8_PEAK_TFLOPS, 4)
+        ent["experts_hit"] = int((counts > 0).sum())
+        if small:
+            flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+            cold = []
+            for i in range(50):
+                flush.fill_(i & 0xFF)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                step()
+                b.record(stream)
+                torch.cuda.synchronize()
+                cold.append(a.elapsed_time(b) * 1e3)
+            ent["cold_cache"] = _pct(cold)
+            del flush
+        table[name] = ent
+        del x, ids, w, w13, w13s, w2, w2s, ws, out, inter, rws, route_out
+        torch.cuda.empty_cache()
+    return table
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the first ~40 layer steps after the GPU leaves idle run up to ~8 % slower
+    # (measured); 50 warm-up steps put the timed steps in the steady state
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the per-workload table (all five layer shapes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with a 1 GiB device-to-device copy, the known-size kernel that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE hardware counters")
@@ -277,6 +390,8 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if not args.no_workloads:
+        rec["workloads"] = workload_table(dev, stream, (x, ids, w, w13, w13s, w2, w2s))
     if args.copy_calibration:
         n = 1 << 30
         src = torch.ones(n, dtype=torch.uint8, device=dev)
