@@ -66,7 +66,7 @@ namespace mxmoe {
 
 namespace {
 
-constexpr int BM = 256;  // token rows per tile
+constexpr int BM = 256;  // token rows per tile (the 128-row variant: kBM below)
 constexpr int BN = 256;  // weight rows per tile
 constexpr int BK = 128;  // K bytes per stage
 constexpr int kThreads = 512;
@@ -104,13 +104,15 @@ struct GmmParams {
 };
 
 constexpr int SK = 128;          // K bytes per stage (whole 128-byte rows)
-constexpr int kSlots = 2;        // LDS ring slots
 
-struct Stage {
+// One ring slot: a k stage of both operands and their scale words, for a
+// tile of kRows token rows.
+template <int kRows>
+struct StageT {
   uint8_t a[BN * SK];
-  uint8_t b[BM * SK];
+  uint8_t b[kRows * SK];
   uint32_t sa[BN];
-  uint32_t sb[BM];
+  uint32_t sb[kRows];
 };
 
 // Group-list types: 0 cumulative, 1 counts (the entry points' two forms);
@@ -137,6 +139,20 @@ __device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t 
   asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(n) for a wave-uniform n (vmcnt(0) above 7): every VMEM
+// instruction but the n latest has completed
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  switch (n) {
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
 // Workgroup barrier that first drains this wave's LDS reads, so no read of a
 // slot can still be pending when the next DMA into that slot is issued.
 __device__ __forceinline__ void barrier() {
@@ -193,13 +209,24 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 // aligned): the first stage of each group of 4 brings 16 bytes per row into
 // a separate double-buffered scale ring, a quarter of the line requests
 // (measured: scale requests cost GEMM1 about a tenth of its time at kG = 1).
-template <bool kSwiglu, bool kW4, int kG>
+// kBM: token rows per tile.  256: the two-slot ring above.  128 (few rows
+// per expert, e.g. decode batches, where the weight stream is latency-bound
+// rather than MFMA-bound): each wave holds one 32-token fragment, a slot is
+// 49.5 KB, and three slots give the DMA two stages of lead; per-stage scale
+// loads only (the scale ring would not fit) and at least 3 k stages.
+template <bool kSwiglu, bool kW4, int kG, int kBM>
 __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   static_assert(kG == 1 || kG == 4, "scale groups of 1 or 4 stages");
+  static_assert(kBM == 256 || (kBM == 128 && kG == 1), "128-row tiles use per-stage scale loads");
+  constexpr int kSl = kBM == 256 ? 2 : 3;   // LDS ring slots
+  constexpr int kNB = kBM / 128;            // 32-token B fragments per wave
+  constexpr int kTokRows = kBM / 8;         // token rows each wave's DMA fetches
+  constexpr int kNT = kTokRows / 8;         // token DMAs per wave per stage
   constexpr int kNA = kW4 ? 2 : 4;          // weight DMAs per wave per stage
-  constexpr int kDmaOps = kNA + 5;          // + 4 token rows + 1 scale load
+  constexpr int kDmaOps = kNA + kNT + 1;    // + 1 scale load
   constexpr int kRowA = kW4 ? SK / 2 : SK;  // weight bytes per LDS row per stage
-  __shared__ __attribute__((aligned(16))) Stage st[kSlots];
+  using Stage = StageT<kBM>;
+  __shared__ __attribute__((aligned(16))) Stage st[kSl];
   __shared__ int s_tile0[kMaxE + 1];
   __shared__ int s_row0[kMaxE + 1];
   // kG = 4: scale words of 4 consecutive stages; group buffer (g/4)%2 holds
@@ -237,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       const int e = lane * PER + i;
       const int64_t r0 = run < p.M ? run : p.M;
       const int64_t r1 = run + n[i] < p.M ? run + n[i] : p.M;
-      tiles[i] = (int)((r1 - r0 + BM - 1) / BM);
+      tiles[i] = (int)((r1 - r0 + kBM - 1) / kBM);
       if (e < E) s_row0[e] = (int)r0;
       if (e == E - 1) s_row0[E] = (int)r1;
       tloc += tiles[i];
@@ -307,15 +334,16 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       if (s_tile0[mid] <= mt) lo = mid; else hi = mid - 1;
     }
     ti.e = uni(lo);
-    ti.m0 = uni64(s_row0[ti.e] + (int64_t)(mt - s_tile0[ti.e]) * BM);
-    ti.rows_valid = uni((int)std::min<int64_t>(BM, s_row0[ti.e + 1] - ti.m0));
+    ti.m0 = uni64(s_row0[ti.e] + (int64_t)(mt - s_tile0[ti.e]) * kBM);
+    ti.rows_valid = uni((int)std::min<int64_t>(kBM, s_row0[ti.e + 1] - ti.m0));
     return ti;
   };
 
   // ---- DMA cursor over the stage sequence (tile j, k stage ks) -------------
-  // wave w fetches rows [32w, 32w+32) of both operands (4 x 8 rows each);
-  // waves 0-3 fetch weight scale rows [64w, 64w+64), waves 4-7 token scale
-  // rows [64(w-4), 64(w-4)+64).  The cursor never passes the last stage: the
+  // wave w fetches weight rows [32w, 32w+32) (4 x 8 rows) and token rows
+  // [kTokRows w, kTokRows (w+1)); waves 0-3 fetch weight scale rows
+  // [64w, 64w+64), waves 4.. token scale rows [64(w-4), 64(w-4)+64) (with
+  // 128-row tiles waves 6 and 7 fetch no scales).  The cursor never passes the last stage: the
   // fetches issued during the last stage repeat it into the slot no wave
   // reads any more, so every fetch is in bounds and the loop has no branch
   // around its loads.
@@ -323,8 +351,8 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     const uint8_t* wrow;   // weight row held in LDS row 32*wave (uniform)
     const uint8_t* arow;   // token row m0 (uniform)
     const uint8_t* srowp;  // scale row base this wave fetches (uniform)
-    int last;              // min(M - 1 - m0, BM - 1): last readable token row of the tile, relative to m0
-    int tok;               // nonzero if this wave's 32 token rows hold a row of the tile's expert
+    int last;              // min(M - 1 - m0, kBM - 1): last readable token row of the tile, relative to m0
+    int tok;               // nonzero if this wave's kTokRows token rows hold a row of the tile's expert
     int rot;               // the tile's k-stage rotation
   };
   auto make_src = [&](int t) __attribute__((always_inline)) -> Src {
@@ -346,8 +374,8 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     s.wrow = uniptr(p.w + (wr + wbase) * (kW4 ? Kd / 2 : Kd));
     s.arow = uniptr(p.a + ti.m0 * Kd);
     s.srowp = wave < 4 ? uniptr(p.ws + (wr + sbase) * srow) : uniptr(p.as + ti.m0 * srow);
-    s.last = uni((int)std::min<int64_t>(p.M - 1 - ti.m0, BM - 1));
-    s.tok = 32 * wave < ti.rows_valid;
+    s.last = uni((int)std::min<int64_t>(p.M - 1 - ti.m0, kBM - 1));
+    s.tok = kTokRows * wave < ti.rows_valid;
     // Tile (expert e, m-tile mt of e, n-tile nt) runs its k stages in the
     // order (nt + mt) % nk, (nt + mt + 1) % nk, ...: tiles that share weight
     // rows (same nt) or token rows (same mt) reach each 128-byte k slice at
@@ -357,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     // order rotated by rot/4 and the stages inside each group rotated by
     // rot%4, so every group is still fetched whole at its first stage.  The
     // accumulation order changes with it, deterministically per tile.
-    s.rot = uni((int)((ti.nt + (ti.m0 - s_row0[ti.e]) / BM) % nk));
+    s.rot = uni((int)((ti.nt + (ti.m0 - s_row0[ti.e]) / kBM) % nk));
     return s;
   };
   // per-lane parts of the DMA offsets
@@ -378,8 +406,10 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     const uint32_t cap = wave < 4 ? 0xffffffffu : (uint32_t)(last * srow);
     return std::min(s_lane, cap);
   };
-  // token rows of this wave's B part: row 32 wave + 8 j + drow, as a byte offset
-  const uint32_t b_row0 = (uint32_t)((32 * wave + drow) * Kd);
+  // token rows of this wave's B part: row kTokRows wave + 8 j + drow, as a byte offset
+  const uint32_t b_row0 = (uint32_t)((kTokRows * wave + drow) * Kd);
+  // waves that fetch scale words (all but 6 and 7 with 128-row tiles)
+  const bool sc_dma = kBM == 256 || wave < 4 + kBM / 64;
   const uint32_t st_base = lds_addr(&st[0]);
   const uint32_t sc_base = lds_addr(&s_sc[0]);
   // memory k stage of tile stage ks for a tile with rotation rot
@@ -395,12 +425,22 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     }
   };
   int cur_r = 0;   // rot % 4 of the tile whose fragments are being read
+  // ring slot of global stage gs
+  auto slot_of = [](int gs) __attribute__((always_inline)) -> int {
+    if constexpr (kSl == 2) return gs & 1;
+    else return (int)((unsigned)gs % 3u);
+  };
+  // VMEM instructions this wave issues for one stage's DMA (kSl = 3: the
+  // mid-stage wait leaves the latest stage in flight; loads retire in order)
+  auto dma_count = [&](const Src& src) __attribute__((always_inline)) -> int {
+    return kNA + (src.tok ? kNT : 0) + (sc_dma ? 1 : 0);
+  };
   const uint32_t s_lds4 = wave < 4 ? (uint32_t)(1024 * wave) : (uint32_t)(4096 + 1024 * (wave - 4));
   // One DMA instruction of k stage ks of the tile whose source is `src`,
   // global stage gs (ring slot gs%2): i = 0..3 weight rows, 4..7 token rows,
   // 8 scales.
   auto dma_part = [&](int i, const Src& src, int ks, int gs) __attribute__((always_inline)) {
-    const uint32_t base = st_base + (uint32_t)(gs & 1) * (uint32_t)sizeof(Stage);
+    const uint32_t base = st_base + (uint32_t)slot_of(gs) * (uint32_t)sizeof(Stage);
     const int kr = kmem(ks, src.rot);   // the k stage in memory
     const uint32_t ko = (uint32_t)(kr * SK);
     // the row and k offsets go into the per-lane 32-bit offset, so the only
@@ -413,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
         dma16(((i & 1) ? lane_off_odd : lane_off_even) + (uint32_t)(8 * i * Kd) + ko, src.wrow,
               base + (uint32_t)offsetof(Stage, a) + (uint32_t)((32 * wave + 8 * i) * SK));
       }
-    } else if (i < kNA + 4) {
+    } else if (i < kNA + kNT) {
       const int j = i - kNA;
       // rows past M repeat the last row
       const uint32_t row = std::min(b_row0 + (uint32_t)(8 * j * Kd), (uint32_t)(src.last * Kd));
@@ -421,9 +461,9 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       // a ragged tail tile skips token rows past its expert's rows: only the
       // outputs of those (never stored) rows read what stays in LDS there
       if (src.tok)
-        dma16(voff, src.arow, base + (uint32_t)offsetof(Stage, b) + (uint32_t)((32 * wave + 8 * j) * SK));
+        dma16(voff, src.arow, base + (uint32_t)offsetof(Stage, b) + (uint32_t)((kTokRows * wave + 8 * j) * SK));
     } else if constexpr (kG == 1) {
-      dma4(s_voff(src.last) + (uint32_t)(kr * 4), src.srowp, base + s_lds);
+      if (sc_dma) dma4(s_voff(src.last) + (uint32_t)(kr * 4), src.srowp, base + s_lds);
     } else if ((ks & 3) == 0) {
       // the group's 16 bytes per row, from its first stage in memory
       dma16(s_voff(src.last) + (uint32_t)((kr & ~3) * 4), src.srowp,
@@ -439,9 +479,9 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   // Fragment rows differ by multiples of 32, so (row/2)%8 = (li/2)%8 for all.
   const int sw = (li >> 1) & 7;
   const uint32_t rd_a = (uint32_t)offsetof(Stage, a) + (uint32_t)((128 * wn + li) * kRowA);
-  const uint32_t rd_b = (uint32_t)offsetof(Stage, b) + (uint32_t)((64 * wm + li) * SK);
+  const uint32_t rd_b = (uint32_t)offsetof(Stage, b) + (uint32_t)((32 * kNB * wm + li) * SK);
   const uint32_t rd_sa = (uint32_t)offsetof(Stage, sa) + (uint32_t)((128 * wn + li) * 4);
-  const uint32_t rd_sb = (uint32_t)offsetof(Stage, sb) + (uint32_t)((64 * wm + li) * 4);
+  const uint32_t rd_sb = (uint32_t)offsetof(Stage, sb) + (uint32_t)((32 * kNB * wm + li) * 4);
   const uint32_t rd_sa4 = (uint32_t)((128 * wn + li) * 16);          // kG = 4 scale ring
   const uint32_t rd_sb4 = (uint32_t)(4096 + (64 * wm + li) * 16);
   uint32_t chk[4];   // byte offset of logical chunk 2c + lg within a row
@@ -473,7 +513,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   };
   // fragments of global stage gs (ring slot gs%2)
   auto load_a = [&](int gs, int s, int f, v8i& frag, int& sc) __attribute__((always_inline)) {
-    const lds_u8* S = slot_ptr(gs & 1);
+    const lds_u8* S = slot_ptr(slot_of(gs));
     const lds_u8* pa = S + rd_a + f * 32 * kRowA;
     if constexpr (kW4) {
       const u32x4 a0 = *reinterpret_cast<lds_u32x4_v*>(pa + chk4[s]);
@@ -489,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       sc = (int)*reinterpret_cast<lds_u8_v*>(group_ptr(gs) + rd_sa4 + f * 512 + 2 * s + lg);
   };
   auto load_b = [&](int gs, int s, int f, v8i& frag, int& sc) __attribute__((always_inline)) {
-    const lds_u8* S = slot_ptr(gs & 1);
+    const lds_u8* S = slot_ptr(slot_of(gs));
     const lds_u8* pb = S + rd_b + f * 32 * SK;
     const u32x4 b0 = *reinterpret_cast<lds_u32x4_v*>(pb + chk[2 * s]);
     const u32x4 b1 = *reinterpret_cast<lds_u32x4_v*>(pb + chk[2 * s + 1]);
@@ -500,19 +540,24 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       sc = (int)*reinterpret_cast<lds_u8_v*>(group_ptr(gs) + rd_sb4 + f * 512 + 2 * s + lg);
   };
   // ---- schedule ---------------------------------------------------------------
-  // Stage g (tile-local k stage ks) lives in slot g%2.  Sub-step 0 of stage g
-  // runs on fragments loaded during the previous sub-step and reloads them
-  // for sub-step 1 from the same slot.  Then one barrier: every wave is done
-  // reading slot g%2 and (after its own vmcnt wait) every part of stage g+1
-  // has landed in the other slot.  Sub-step 1 reloads the fragments of stage
-  // g+1's sub-step 0 and, after its first two MFMAs, issues the DMA of stage
-  // g+2 into slot g%2, a full stage ahead of its use.  A tile's last stage
-  // issues no DMA: its slot holds the epilogue's staging, and the DMA that
-  // was skipped follows the epilogue.
+  // Stage g (tile-local k stage ks) lives in slot g%S (S = kSl slots).
+  // Sub-step 0 of stage g runs on fragments loaded during the previous
+  // sub-step and reloads them for sub-step 1 from the same slot.  Then one
+  // barrier: every wave is done reading slot g%S and (after its own vmcnt
+  // wait) every part of stage g+1 has landed.  Sub-step 1 reloads the
+  // fragments of stage g+1's sub-step 0 and, after its first two MFMAs,
+  // issues the DMA of stage g+S into slot g%S, S-1 stages ahead of its use
+  // (with S = 3 the wait leaves that latest DMA in flight).  A tile's last
+  // stage issues no DMA: its slot holds the epilogue's staging, and the DMA
+  // that was skipped follows the epilogue.
 
-  // prologue: stages 0 and 1 in flight
+  // prologue: stages 0 .. S-1 in flight
   const Src first = make_src(xcd_base);
-  if (nk > 1) {
+  if constexpr (kSl == 3) {   // nk >= 3 (host)
+    dma_stage(first, 0, 0);
+    dma_stage(first, 1, 1);
+    dma_stage(first, 2, 2);
+  } else if (nk > 1) {
     dma_stage(first, 0, 0);
     dma_stage(first, 1, 1);
   } else {
@@ -522,32 +567,35 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   wait_vmcnt0();
   barrier();
 
-  int g = 0;   // global stage index
+  int g = 0;          // global stage index
+  int last_cnt = 0;   // kSl = 3: VMEM instructions of this wave's latest stage DMA
   for (int cj = 0; cj < my_tiles; ++cj) {
     const TileInfo cur = tile_info(cj * TS + xcd_base);
-    // Ragged tail tiles: a wave whose 64 tokens are all past the expert's
-    // rows computes nothing (no fragment loads, MFMAs or epilogue work); it
-    // still issues its share of the weight DMA and meets every barrier.
-    const bool active = 64 * wm < cur.rows_valid;
+    // Ragged tail tiles: a wave whose 32 kNB tokens are all past the
+    // expert's rows computes nothing (no fragment loads, MFMAs or epilogue
+    // work); it still issues its share of the weight DMA and meets every
+    // barrier.
+    const bool active = 32 * kNB * wm < cur.rows_valid;
     const Src csrc = make_src(cj * TS + xcd_base);
     cur_r = csrc.rot & 3;
     const bool has_next = cj + 1 < my_tiles;
     const Src nsrc = has_next ? make_src((cj + 1) * TS + xcd_base) : csrc;
-    v8i fa[4], fb[2];
-    int sa[4], sb[2];
-    v16f acc[4][2];
-    // The 8 MFMAs of one sub-step, B fragment 0 with A fragments 0..3, then B
-    // fragment 1 with A 0..3.  Each fragment is reloaded for the next sub-step
-    // (stage `nstage`, sub-step `ns`) right after its last MFMA, so the LDS reads
-    // overlap the matrix work; `extra(m)` runs after MFMA m (DMA issue).
+    v8i fa[4], fb[kNB];
+    int sa[4], sb[kNB];
+    v16f acc[4][kNB];
+    // The 4 kNB MFMAs of one sub-step, B fragment 0 with A fragments 0..3,
+    // then B fragment 1 with A 0..3.  Each fragment is reloaded for the next
+    // sub-step (stage `nstage`, sub-step `ns`) right after its last MFMA, so
+    // the LDS reads overlap the matrix work; `extra(m)` runs after MFMA m
+    // (DMA issue).
     auto substep = [&](int nstage, int ns, auto kReload, auto extra) __attribute__((always_inline)) {
       if (!active) {
   #pragma unroll
-        for (int m = 0; m < 8; ++m) extra(m);
+        for (int m = 0; m < 4 * kNB; ++m) extra(m);
         return;
       }
   #pragma unroll
-      for (int m = 0; m < 8; ++m) {
+      for (int m = 0; m < 4 * kNB; ++m) {
         const int fm = m >> 2, fn = m & 3;
         // A format 4 = e2m1 (W4A8), 0 = e4m3; B (tokens) is always e4m3
         acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[fn], fb[fm], acc[fn][fm], kW4 ? 4 : 0, 0, 0,
@@ -558,9 +606,14 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
         asm volatile("" : "+v"(acc[fn][fm]));
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (decltype(kReload)::value) {
-          if (m == 3) load_b(nstage, ns, 0, fb[0], sb[0]);
-          if (m >= 4) load_a(nstage, ns, m - 4, fa[m - 4], sa[m - 4]);
-          if (m == 7) load_b(nstage, ns, 1, fb[1], sb[1]);
+          if constexpr (kNB == 2) {
+            if (m == 3) load_b(nstage, ns, 0, fb[0], sb[0]);
+            if (m >= 4) load_a(nstage, ns, m - 4, fa[m - 4], sa[m - 4]);
+            if (m == 7) load_b(nstage, ns, 1, fb[1], sb[1]);
+          } else {
+            load_a(nstage, ns, m, fa[m], sa[m]);
+            if (m == 3) load_b(nstage, ns, 0, fb[0], sb[0]);
+          }
         }
         extra(m);
         __builtin_amdgcn_sched_barrier(0);
@@ -570,28 +623,30 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   #pragma unroll
       for (int f = 0; f < 4; ++f) load_a(gs, s, f, fa[f], sa[f]);
   #pragma unroll
-      for (int f = 0; f < 2; ++f) load_b(gs, s, f, fb[f], sb[f]);
+      for (int f = 0; f < kNB; ++f) load_b(gs, s, f, fb[f], sb[f]);
     };
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < kNB; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
     // the tile's first fragments (stage g has landed: the prologue's barrier,
     // or the middle barrier of the previous tile's last stage)
     if (active) load_all(g, 0);
 
-    // one k stage; kDma: issue stage g+2's DMA (every stage but the tile's last)
+    // one k stage; kDma: issue stage g+S's DMA (every stage but the tile's last)
     auto stage = [&](int ks, auto kDma) __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
       substep(g, 1, std::true_type{}, [&](int) {});
-      wait_vmcnt0();   // this wave's part of stage g+1 has landed
-      barrier();       // every wave's has, and nobody reads slot g%2 any more
+      // this wave's part of stage g+1 has landed (S = 3: stage g+2's DMA,
+      // the latest, may still be in flight)
+      if constexpr (kSl == 2) wait_vmcnt0(); else wait_vmcnt_le(last_cnt);
+      barrier();       // every wave's has, and nobody reads slot g%S any more
       if constexpr (decltype(kDma)::value) {
-        // DMA target: stage ks+2 of this tile, else stage 0 of the next tile,
-        // else (last tile) a repeat of this tile's last stage, never read
-        const bool in_tile = ks + 2 < nk;
+        // DMA target: stage ks+S of this tile, else stage ks+S-nk of the next
+        // tile, else (last tile) a repeat of this tile's last stage, never read
+        const bool in_tile = ks + kSl < nk;
         Src t;
         t.wrow = in_tile ? csrc.wrow : nsrc.wrow;
         t.arow = in_tile ? csrc.arow : nsrc.arow;
@@ -599,19 +654,21 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
         t.last = in_tile ? csrc.last : nsrc.last;
         t.tok = in_tile ? csrc.tok : nsrc.tok;
         t.rot = in_tile ? csrc.rot : nsrc.rot;
-        const int tks = in_tile ? ks + 2 : (has_next ? 0 : nk - 1);
+        // (S = 2: only stage nk-2 reaches past the tile, to the next tile's stage 0)
+        const int tks = in_tile ? ks + kSl : (has_next ? (kSl == 2 ? 0 : ks + kSl - nk) : nk - 1);
         // the DMA goes out early in the sub-step (measured: issuing it over
         // all eight MFMAs leaves the last loads too little time to land)
         substep(g + 1, 0, std::true_type{}, [&](int m) __attribute__((always_inline)) {
           if (m == 0) {
 #pragma unroll
-            for (int i = 0; i < 5; ++i) dma_part(i, t, tks, g + 2);
+            for (int i = 0; i < 5; ++i) dma_part(i, t, tks, g + kSl);
           }
           if (m == 1) {
 #pragma unroll
-            for (int i = 5; i < kDmaOps; ++i) dma_part(i, t, tks, g + 2);
+            for (int i = 5; i < kDmaOps; ++i) dma_part(i, t, tks, g + kSl);
           }
         });
+        if constexpr (kSl == 3) last_cnt = dma_count(t);
       } else {
         substep(g + 1, 0, std::false_type{}, [&](int) {});   // the next tile reloads at its start
       }
@@ -630,15 +687,22 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       // them back row-contiguous.  Staging layout: token row r at r*256;
       // 16-byte chunk c at physical chunk c ^ (r%16), and its two 8-byte
       // halves swapped when r >= 16, so both the writes (lane = token) and
-      // the reads (16 lanes per row) are free of bank conflicts.
+      // the reads (16 lanes per row) are free of bank conflicts.  With
+      // 128-row tiles the 8 KB per wave do not fit one 49.5 KB slot for all
+      // 8 waves: waves 0-3 go first, then (after a barrier) waves 4-7 reuse
+      // the same regions.
       const int64_t N = p.Nw;
-      if (active) {
+      constexpr int kRounds = kBM == 256 ? 1 : 2;
+#pragma unroll
+      for (int round = 0; round < kRounds; ++round) {
+      if (kRounds == 2 && round == 1) barrier();   // round 0's read-backs are done
+      if (active && (kRounds == 1 || (wave >> 2) == round)) {
       const int li = opaque(lane & 31), lg = opaque(lane >> 5), lane_e = opaque(lane);
-      lds_u8* stg = (lds_u8*)(uintptr_t)(st_base + (uint32_t)((g - 1) & 1) * (uint32_t)sizeof(Stage) +
-                                         (uint32_t)(wave * 8192));
+      lds_u8* stg = (lds_u8*)(uintptr_t)(st_base + (uint32_t)slot_of(g - 1) * (uint32_t)sizeof(Stage) +
+                                         (uint32_t)((kRounds == 1 ? wave : (wave & 3)) * 8192));
       const int rr = lane_e >> 4, rc = lane_e & 15;   // read-back: row within a group of 4, chunk
 #pragma unroll
-      for (int fm = 0; fm < 2; ++fm) {
+      for (int fm = 0; fm < kNB; ++fm) {
 #pragma unroll
         for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
@@ -657,7 +721,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
           v[it] = *reinterpret_cast<lds_u32x4*>(stg + r * 256 + ((rc ^ (r & 15)) << 4));
           if (it >= 4) v[it] = u32x4{v[it].z, v[it].w, v[it].x, v[it].y};   // rows 16-31
         }
-        const int mc0 = 64 * wm + 32 * fm + rr;
+        const int mc0 = 32 * kNB * wm + 32 * fm + rr;
         uint16_t* y0 = p.y + (cur.m0 + mc0) * N + (int64_t)cur.nt * BN + 128 * wn + 8 * rc;
 #pragma unroll
         for (int it = 0; it < 8; ++it)
@@ -666,23 +730,25 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
         asm volatile("" ::: "memory");   // a wave's LDS accesses execute in issue order
       }
       }   // active
+      }   // round
     } else {
       // SwiGLU, MX requant, and the stores through LDS: the two waves that
-      // share a 64-token block (wn = 0, 1: 64 h columns each) stage their
-      // e4m3 bytes into one 64 x 128-byte region (16-byte chunk index
-      // XOR-ed with (row/2)%8) and their scale bytes into 64 x 4 bytes, so
-      // after a barrier every row of the tile leaves as one full 128-byte
-      // line and one 4-byte scale word.
+      // share a block of kTB = 32 kNB tokens (wn = 0, 1: 64 h columns each)
+      // stage their e4m3 bytes into one kTB x 128-byte region (16-byte chunk
+      // index XOR-ed with (row/2)%8) and their scale bytes into kTB x 4
+      // bytes, so after a barrier every row of the tile leaves as one full
+      // 128-byte line and one 4-byte scale word.
+      constexpr int kTB = 32 * kNB;
       const int64_t I = p.I;
       const int li = opaque(lane & 31), lg = opaque(lane >> 5), lane_e = opaque(lane);
-      lds_u8* grp = (lds_u8*)(uintptr_t)(st_base + (uint32_t)((g - 1) & 1) * (uint32_t)sizeof(Stage) +
-                                         (uint32_t)(wm * (64 * 128 + 64 * 4)));
-      lds_u8* grp_s = grp + 64 * 128;
+      lds_u8* grp = (lds_u8*)(uintptr_t)(st_base + (uint32_t)slot_of(g - 1) * (uint32_t)sizeof(Stage) +
+                                         (uint32_t)(wm * (kTB * 128 + kTB * 4)));
+      lds_u8* grp_s = grp + kTB * 128;
       // (both waves of a group are active or neither: they share wm)
 #pragma unroll
-      for (int fm = 0; fm < 2; ++fm) {
+      for (int fm = 0; fm < kNB; ++fm) {
         if (!active) break;
-        const int t = 32 * fm + li;   // token row within the 64-token block
+        const int t = 32 * fm + li;   // token row within the kTB-token block
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           __builtin_amdgcn_sched_barrier(0);   // one 32x32 block at a time
@@ -705,8 +771,8 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
                 e4m3x4(h[4 * q] * inv, h[4 * q + 1] * inv, h[4 * q + 2] * inv, h[4 * q + 3] * inv);
           }
           if (lg == 0) grp_s[t * 4 + 2 * wn + f] = static_cast<uint8_t>(sbyte);
-          if (p.hdbg && 64 * wm + t < cur.rows_valid) {
-            float* drow_ = p.hdbg + (cur.m0 + 64 * wm + t) * I + (int64_t)cur.nt * (BN / 2) + 64 * wn + 32 * f;
+          if (p.hdbg && kTB * wm + t < cur.rows_valid) {
+            float* drow_ = p.hdbg + (cur.m0 + kTB * wm + t) * I + (int64_t)cur.nt * (BN / 2) + 64 * wn + 32 * f;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               *reinterpret_cast<float4*>(drow_ + 8 * q + 4 * lg) =
@@ -715,31 +781,37 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
         }
       }
       barrier();
-      // wave wn stores rows [32 wn, 32 wn + 32) of its group: 8 lanes per row
+      // wave wn stores rows [kTB/2 wn, kTB/2 (wn + 1)) of its group: 8 lanes per row
       if (active) {
+      constexpr int kHR = kTB / 2;   // rows per wave
       const int64_t hc0 = (int64_t)cur.nt * (BN / 2);
-      u32x4 v[4];
+      u32x4 v[kHR / 8];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int r = 32 * wn + 8 * it + (lane_e >> 3);
+      for (int it = 0; it < kHR / 8; ++it) {
+        const int r = kHR * wn + 8 * it + (lane_e >> 3);
         v[it] = *reinterpret_cast<lds_u32x4*>(grp + r * 128 + ((((lane_e & 7) ^ ((r >> 1) & 7))) << 4));
       }
-      const uint32_t sw_word = li < 32 ? *reinterpret_cast<lds_u32*>(grp_s + (32 * wn + li) * 4) : 0u;
+      const uint32_t sw_word = li < kHR ? *reinterpret_cast<lds_u32*>(grp_s + (kHR * wn + li) * 4) : 0u;
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int r = 32 * wn + 8 * it + (lane_e >> 3);
-        if (64 * wm + r < cur.rows_valid)
-          *reinterpret_cast<u32x4*>(p.hq + (cur.m0 + 64 * wm + r) * I + hc0 + 16 * (lane_e & 7)) = v[it];
+      for (int it = 0; it < kHR / 8; ++it) {
+        const int r = kHR * wn + 8 * it + (lane_e >> 3);
+        if (kTB * wm + r < cur.rows_valid)
+          *reinterpret_cast<u32x4*>(p.hq + (cur.m0 + kTB * wm + r) * I + hc0 + 16 * (lane_e & 7)) = v[it];
       }
-      if (lg == 0 && 64 * wm + 32 * wn + li < cur.rows_valid)
-        *reinterpret_cast<uint32_t*>(p.hs + (cur.m0 + 64 * wm + 32 * wn + li) * (I / 32) + hc0 / 32) = sw_word;
+      if (lg == 0 && (kHR == 32 || li < kHR) && kTB * wm + kHR * wn + li < cur.rows_valid)
+        *reinterpret_cast<uint32_t*>(p.hs + (cur.m0 + kTB * wm + kHR * wn + li) * (I / 32) + hc0 / 32) = sw_word;
       }   // active
     }
     // every wave is done with the staging slot: issue the DMA the last stage
-    // skipped, global stage g + 1 (the next tile's stage 1, or with one stage
-    // per tile the stage 0 of the tile after next)
+    // skipped, global stage g + S - 1 (the next tile's stage S - 1, or with
+    // one stage per tile the stage 0 of the tile after next)
     barrier();
-    if (nk > 1) {
+    if constexpr (kSl == 3) {
+      if (has_next) {
+        dma_stage(nsrc, 2, g + 2);
+        last_cnt = dma_count(nsrc);
+      }
+    } else if (nk > 1) {
       if (has_next) dma_stage(nsrc, 1, g + 1);
     } else if (cj + 2 < my_tiles) {
       dma_stage(make_src((cj + 2) * TS + xcd_base), 0, g + 1);
@@ -749,22 +821,35 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   wait_vmcnt0();
 }
 
+// 128-row tiles (three-slot ring) when the experts average at most this
+// many rows, where a 256-row tile is at most a quarter full and the GEMMs
+// stream weights rather than compute.  Measured on the layer: decode
+// (2 rows per expert) 157 -> 138 us; at 128 rows per expert (T = 2048,
+// top-8 of 128) the 128-row tiles were 2 % slower.
+constexpr int64_t kSmallRowsPerExpert = 64;
+
 template <bool kSwiglu, bool kW4>
 int launch(const GmmParams& p, hipStream_t stream, const char* name) {
   if (p.M == 0) return MX_OK;
-  const int64_t upper = ((p.M + BM - 1) / BM + p.E) * (int64_t)p.n_tiles;
+  const bool small = p.Kd / BK >= 3 && p.gl_type != kGlSingle && p.M <= kSmallRowsPerExpert * p.E;
+  const int64_t bm = small ? 128 : BM;
+  const int64_t upper = ((p.M + bm - 1) / bm + p.E) * (int64_t)p.n_tiles;
   if (upper >= ((int64_t)1 << 31)) return fail(MX_ERR_UNSUPPORTED, "%s: too many tiles", name);
   int64_t grid = (int64_t)num_cus() / 8 * 8;
   if (grid < 8) grid = 8;
   if (grid > (upper + 7) / 8 * 8) grid = (upper + 7) / 8 * 8;
+  if (small) {
+    gmm_kernel<kSwiglu, kW4, 1, 128><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    return check_launch(name);
+  }
   // scale groups of 4 stages when the k stages divide into them and both
   // scale tensors are 16-byte aligned (every scale row then is)
   const bool groups = (p.Kd / BK) % 4 == 0 && reinterpret_cast<uintptr_t>(p.as) % 16 == 0 &&
                       reinterpret_cast<uintptr_t>(p.ws) % 16 == 0;
   if (groups)
-    gmm_kernel<kSwiglu, kW4, 4><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    gmm_kernel<kSwiglu, kW4, 4, 256><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
   else
-    gmm_kernel<kSwiglu, kW4, 1><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    gmm_kernel<kSwiglu, kW4, 1, 256><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
   return check_launch(name);
 }
 

@@ -208,6 +208,10 @@ def _mx_operands(M, Kd, E, N, spread=4):
     return aq, as_, wq.reshape(E, N, Kd), ws.reshape(E, N, -1, 2)
 
 
+# The library picks 128-token tiles (three-slot ring) when Kd >= 384 and the
+# experts average at most 64 rows (M <= 64 E), else 256-token tiles: here
+# the *-128, small-tiles-3stage and decode-like cases (empty experts appended
+# where needed) take the 128-row kernel, the rest the 256-row one.
 GMM_CASES = {
     "ragged": ([0, 1, 127, 128, 129, 255, 256, 257, 300, 0, 5], 256, 256),
     "single-expert": ([515], 384, 256),
@@ -218,6 +222,14 @@ GMM_CASES = {
     # 64-token boundary (waves skip MFMAs / token DMA); K = 512 runs the
     # 4-stage scale groups
     "tail-boundaries": ([64, 65, 192, 193, 32, 33, 128, 1], 512, 256),
+    # the same tails with one large expert: 256-row tiles, 4-stage scale groups
+    "tail-boundaries-256": ([64, 65, 192, 193, 32, 33, 128, 1, 2000], 512, 256),
+    # the same tails on 128-row tiles
+    "tail-boundaries-128": ([64, 65, 192, 193, 32, 33, 128, 1] + [0] * 4, 512, 256),
+    # 128-row tiles with the fewest k stages (3) and tails at 16/32/128 rows
+    "small-tiles-3stage": ([16, 17, 31, 32, 33, 127, 128, 129, 0, 255, 1] + [0] * 2, 384, 512),
+    # decode-shaped: many experts of 0-4 rows, 6 k stages
+    "decode-like": ([2, 3, 0, 1, 2, 2, 0, 4] * 8, 768, 256),
 }
 
 
@@ -296,11 +308,16 @@ def test_gmm_mx_guard_bands_and_untouched_rows():
     assert np.all(yh[199:] == 0x5A5A)                  # rows past the last expert untouched
 
 
+# (128-row tiles: single, tail-boundaries-128, small-tiles-3stage, decode-like)
 GMM1_CASES = {
     "ragged": ([3, 0, 128, 129, 1, 260, 256, 511], 256, 128),
     "wide-i": ([70, 150], 128, 384),
     "single": ([1], 512, 128),
     "tail-boundaries": ([64, 65, 192, 193, 32, 33, 1], 512, 128),
+    "tail-boundaries-256": ([64, 65, 192, 193, 32, 33, 1, 1500], 512, 128),
+    "tail-boundaries-128": ([64, 65, 192, 193, 32, 33, 1] + [0] * 3, 512, 128),
+    "small-tiles-3stage": ([16, 17, 31, 32, 33, 127, 128, 129, 0, 255, 1] + [0] * 2, 384, 256),
+    "decode-like": ([2, 3, 0, 1, 2, 2, 0, 4] * 8, 2048, 128),
 }
 
 

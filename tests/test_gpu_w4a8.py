@@ -81,6 +81,8 @@ W4_GMM_CASES = {
     "single-expert": ([515], 384, 256),
     "wide-k": ([64, 200, 33], 1024, 256),
     "multi-tile-n": ([700, 20], 256, 768),
+    # 128-row tiles (three-slot ring): 3 k stages, tails at 16/32/128 rows
+    "small-tiles-3stage": ([16, 33, 129, 0, 255] + [0] * 2, 384, 256),
 }
 
 
@@ -119,6 +121,8 @@ def test_gmm_mx_w4a8_exact_case():
 W4_GMM1_CASES = {
     "ragged": ([3, 0, 128, 129, 1, 260, 256, 511], 256, 128),
     "wide-i": ([70, 150], 128, 384),
+    # 128-row tiles (three-slot ring)
+    "small-tiles-3stage": ([16, 17, 31, 33, 127, 129, 1], 384, 128),
 }
 
 
