@@ -230,6 +230,8 @@ GMM_CASES = {
     "small-tiles-3stage": ([16, 17, 31, 32, 33, 127, 128, 129, 0, 255, 1] + [0] * 2, 384, 512),
     # decode-shaped: many experts of 0-4 rows, 6 k stages
     "decode-like": ([2, 3, 0, 1, 2, 2, 0, 4] * 8, 768, 256),
+    # 512 tiles, two per CU: the ring carries across tile boundaries
+    "decode-many-tiles": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 384, 1024),
 }
 
 
@@ -318,6 +320,8 @@ GMM1_CASES = {
     "tail-boundaries-128": ([64, 65, 192, 193, 32, 33, 1] + [0] * 3, 512, 128),
     "small-tiles-3stage": ([16, 17, 31, 32, 33, 127, 128, 129, 0, 255, 1] + [0] * 2, 384, 256),
     "decode-like": ([2, 3, 0, 1, 2, 2, 0, 4] * 8, 2048, 128),
+    # 512 tiles, two per CU: the ring carries across tile boundaries
+    "decode-many-tiles": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 384, 512),
 }
 
 
