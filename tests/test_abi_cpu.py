@@ -83,8 +83,10 @@ def test_gmm_validation(lib):
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 256, 96, 4, FAKE, None) == UNSUPPORTED   # Kd % 128
     assert g(FAKE, FAKE, FAKE, FAKE, None, 1, 16, 256, 128, 4, FAKE, None) == INVALID     # null group list
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 256, 128, 0, FAKE, None) == INVALID     # E = 0
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 256, 128, 1025, FAKE, None) == UNSUPPORTED  # E > 1024
     s = lib.gmm_swiglu_mxquant
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 64, 4, FAKE, FAKE, None, None) == UNSUPPORTED  # I % 128
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 128, 1025, FAKE, FAKE, None, None) == UNSUPPORTED  # E > 1024
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 16, 128, 128, 4, FAKE, FAKE, None, None) == INVALID
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 128, 128, 4, None, FAKE, None, None) == INVALID
 

@@ -353,6 +353,46 @@ def test_gmm_swiglu_mxquant_parity(name):
     assert np.array_equal(host(hq0), host(hq)) and np.array_equal(host(hs0), host(hs))
 
 
+def _checkpoint_bytes(rng, shape):
+    """Random e4m3 weight bytes (NaN codes 0x7F/0xFF moved to 0x7E/0xFE) and
+    scale bytes in 118..121, as a pre-quantised checkpoint ships them."""
+    n = int(np.prod(shape))
+    q = np.frombuffer(rng.bytes(n), np.uint8).copy()
+    q[(q & 0x7F) == 0x7F] &= 0xFE
+    s = rng.integers(118, 122, size=shape[:-1] + (shape[-1] // 64, 2), dtype=np.uint8)
+    return q.reshape(shape), s
+
+
+@pytest.mark.parametrize("kd", [256, 384])
+def test_gmm_max_experts(kd):
+    """Both GEMMs at the largest expert count the kernels take (1024), with
+    0-3 rows per expert: Kd = 256 runs the 256-row tiles, Kd = 384 the
+    128-row tiles with the three-slot ring."""
+    rng = np.random.default_rng(1024 + kd)
+    E, N, I = 1024, 256, 128
+    counts = rng.integers(0, 4, E).astype(np.int64)
+    M = int(counts.sum())
+    say(f"gmm_mx / gmm_swiglu_mxquant E={E} M={M} Kd={kd}")
+    aq, as_ = mx_ref.mx_quantize_ref(rng.standard_normal((M, kd)))
+    wq, ws = _checkpoint_bytes(rng, (E, N, kd))
+    y = mx.gmm_mx(u8_dev(aq), u8_dev(as_), u8_dev(wq), u8_dev(ws), i64_dev(counts), 1)
+    torch.cuda.synchronize()
+    err = bf16_rows_rel_err(bf16_host(y), moe_ref.gmm_mx_ref(aq, as_, wq, ws, counts, 1))
+    say(f"  gmm_mx max row rel err {err.max():.3g}")
+    assert err.max() <= TOL
+    w13q, w13s = _checkpoint_bytes(rng, (E, 2 * I, kd))
+    hq, hs, h = mx.gmm_swiglu_mxquant(u8_dev(aq), u8_dev(as_), u8_dev(w13q), u8_dev(w13s), i64_dev(counts), 1,
+                                      h_debug=True)
+    torch.cuda.synchronize()
+    rq, rs, rh = moe_ref.gmm_swiglu_mxquant_ref(aq, as_, w13q, w13s, counts, 1, I)
+    hk = host(h)
+    herr = row_rel_err(hk, rh)
+    say(f"  gmm_swiglu_mxquant h max row rel err {herr.max():.3g}")
+    assert herr.max() <= 1e-3
+    kq, ks = mx_ref.mx_quantize_ref(hk.astype(np.float64))
+    assert np.array_equal(host(hq), kq) and np.array_equal(host(hs), ks)
+
+
 def _offset_u8_dev(a, offset=4):
     """uint8 device copy whose data pointer is 4 bytes past a 256-byte
     aligned allocation: 4-byte aligned, not 16-byte aligned."""
