@@ -19,7 +19,9 @@ object is computed from those.  The top-k router upstream of the layer
 dense MXFP8 linear layer (mx_linear, T=16384, K=N=4096, offline-style
 pre-quantised weight): a second workload of the same MX GEMM, not part of
 the MoE step.  And so is the same 16K prefill layer with MXFP4 (e2m1) expert
-weights (moe_w4a8_forward), with its two GEMMs timed separately.  Last, the
+weights (moe_w4a8_forward), with its two GEMMs timed separately; and so is
+the load-time weight quantisation (mx_quantize and mx_quantize_fp4 on bf16
+weights of w13's shape).  Last, the
 "workloads" object times the layer on all five shapes (tiny, decode, mid,
 16K prefill, wide prefill): per-step median/p10/p90, tokens/s, per-kernel
 medians and the GEMMs' TFLOP/s, plus cold-cache steps for the two small
@@ -323,6 +325,34 @@ def main():
                                "hbm_GBs": round(l_bytes / l_dur / 1e9, 1), "alg_bytes": int(l_bytes),
                                "alg_flops": int(l_flops), "in_step": False}
     del lx, lwq, lws, ly, lws_buf
+
+    # ---- load-time weight quantisation (outside the step) ---------------------
+    # bf16 weights of w13's shape [E, 2I, K], N(0, 0.02), drawn on the device
+    # from a seeded generator; mx_quantize (e4m3) and mx_quantize_fp4 (e2m1)
+    # each read 2 bytes per element and write the payload plus one scale byte
+    # per 32 elements.
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    wb = (torch.randn((E * 2 * I, K), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    nel = wb.numel()
+    for name, fn, payload in (("mx_quantize_weights", mx.mx_quantize, 1.0),
+                              ("mx_quantize_fp4_weights", mx.mx_quantize_fp4, 0.5)):
+        qo, so = fn(wb)
+        for _ in range(3):
+            fn(wb, q=qo, s=so)
+        rev[0].record(stream)
+        for _ in range(args.steps):
+            fn(wb, q=qo, s=so)
+        rev[1].record(stream)
+        torch.cuda.synchronize()
+        q_dur = rev[0].elapsed_time(rev[1]) * 1e-3 / args.steps
+        q_bytes = nel * (2 + payload + 1 / 32)
+        kernels[name] = {"avg_us": round(q_dur * 1e6, 2), "rows": E * 2 * I, "cols": K,
+                         "hbm_GBs": round(q_bytes / q_dur / 1e9, 1),
+                         "hbm_frac": round(q_bytes / q_dur / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": int(q_bytes),
+                         "in_step": False}
+        del qo, so
+    del wb
 
     # ---- the same layer with MXFP4 (e2m1) expert weights (W4A8) -------------
     # The mixed e2m1 x e4m3 block-scaled MFMA issues at the fp8 rate, so the
