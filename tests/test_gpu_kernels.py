@@ -210,7 +210,7 @@ def _mx_operands(M, Kd, E, N, spread=4):
 
 # The library picks 128-token tiles (three-slot ring) when Kd >= 384 and the
 # experts average at most 64 rows (M <= 64 E), else 256-token tiles: here
-# the *-128, small-tiles-3stage and decode-like cases (empty experts appended
+# the *-128, *-3stage, *-4stage and decode-* cases (empty experts appended
 # where needed) take the 128-row kernel, the rest the 256-row one.
 GMM_CASES = {
     "ragged": ([0, 1, 127, 128, 129, 255, 256, 257, 300, 0, 5], 256, 256),
@@ -232,6 +232,9 @@ GMM_CASES = {
     "decode-like": ([2, 3, 0, 1, 2, 2, 0, 4] * 8, 768, 256),
     # 512 tiles, two per CU: the ring carries across tile boundaries
     "decode-many-tiles": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 384, 1024),
+    # 128-row tiles with 4 k stages: tails at 16/32/128 rows; 1024 tiles
+    "small-tiles-4stage": ([16, 17, 31, 32, 33, 127, 128, 129, 0, 255, 1] + [0] * 2, 512, 512),
+    "decode-many-tiles-4stage": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 512, 1024),
 }
 
 
@@ -310,7 +313,7 @@ def test_gmm_mx_guard_bands_and_untouched_rows():
     assert np.all(yh[199:] == 0x5A5A)                  # rows past the last expert untouched
 
 
-# (128-row tiles: single, tail-boundaries-128, small-tiles-3stage, decode-like)
+# (128-row tiles: single, tail-boundaries-128, *-3stage, *-4stage, decode-*)
 GMM1_CASES = {
     "ragged": ([3, 0, 128, 129, 1, 260, 256, 511], 256, 128),
     "wide-i": ([70, 150], 128, 384),
@@ -322,6 +325,8 @@ GMM1_CASES = {
     "decode-like": ([2, 3, 0, 1, 2, 2, 0, 4] * 8, 2048, 128),
     # 512 tiles, two per CU: the ring carries across tile boundaries
     "decode-many-tiles": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 384, 512),
+    "small-tiles-4stage": ([16, 17, 31, 32, 33, 127, 128, 129, 0, 255, 1] + [0] * 2, 512, 256),
+    "decode-many-tiles-4stage": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 512, 512),
 }
 
 
@@ -363,11 +368,11 @@ def _checkpoint_bytes(rng, shape):
     return q.reshape(shape), s
 
 
-@pytest.mark.parametrize("kd", [256, 384])
+@pytest.mark.parametrize("kd", [256, 384, 512])
 def test_gmm_max_experts(kd):
     """Both GEMMs at the largest expert count the kernels take (1024), with
-    0-3 rows per expert: Kd = 256 runs the 256-row tiles, Kd = 384 the
-    128-row tiles with the three-slot ring."""
+    0-3 rows per expert: Kd = 256 runs the 256-row tiles, Kd = 384 and 512
+    the 128-row tiles with the three-slot ring (3 and 4 k stages)."""
     rng = np.random.default_rng(1024 + kd)
     E, N, I = 1024, 256, 128
     counts = rng.integers(0, 4, E).astype(np.int64)

@@ -83,6 +83,7 @@ W4_GMM_CASES = {
     "multi-tile-n": ([700, 20], 256, 768),
     # 128-row tiles (three-slot ring): 3 k stages, tails at 16/32/128 rows
     "small-tiles-3stage": ([16, 33, 129, 0, 255] + [0] * 2, 384, 256),
+    "small-tiles-4stage": ([16, 33, 129, 0, 255] + [0] * 2, 512, 256),
 }
 
 
@@ -123,6 +124,7 @@ W4_GMM1_CASES = {
     "wide-i": ([70, 150], 128, 384),
     # 128-row tiles (three-slot ring)
     "small-tiles-3stage": ([16, 17, 31, 33, 127, 129, 1], 384, 128),
+    "small-tiles-4stage": ([16, 17, 31, 33, 127, 129, 1], 512, 128),
 }
 
 
