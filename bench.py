@@ -95,7 +95,13 @@ def cpu_baseline(d, tokens=2048):
     moe_ref.moe_forward_ref(d["x"][:tokens], d["topk_ids"][:tokens], d["topk_w"][:tokens], d["w13q"], d["w13s"],
                             d["w2q"], d["w2s"])
     dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "cpu": cpu, "kind": "oracle",
             "sample": f"first {tokens} of {CFG.T} tokens of the same workload (all {CFG.E} experts), "
                       f"full oracle layer, {dt:.1f} s"}
 
