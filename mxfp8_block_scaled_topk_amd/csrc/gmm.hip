@@ -377,16 +377,20 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     s.srowp = wave < 4 ? uniptr(p.ws + (wr + sbase) * srow) : uniptr(p.as + ti.m0 * srow);
     s.last = uni((int)std::min<int64_t>(p.M - 1 - ti.m0, kBM - 1));
     s.tok = kTokRows * wave < ti.rows_valid;
-    // Tile (expert e, m-tile mt of e, n-tile nt) runs its k stages in the
-    // order (nt + mt) % nk, (nt + mt + 1) % nk, ...: tiles that share weight
-    // rows (same nt) or token rows (same mt) reach each 128-byte k slice at
-    // different times, so one of them takes the L2 miss and the others hit
-    // (measured: GEMM2 17 % faster, GEMM1 3 %, at the 16K prefill size).
-    // With scale groups (kG = 4) the groups of 4 stages are visited in an
-    // order rotated by rot/4 and the stages inside each group rotated by
-    // rot%4, so every group is still fetched whole at its first stage.  The
-    // accumulation order changes with it, deterministically per tile.
-    s.rot = uni((int)((ti.nt + (ti.m0 - s_row0[ti.e]) / kBM) % nk));
+    // GEMM2: tile (expert e, m-tile mt of e, n-tile nt) runs its k stages in
+    // the order (nt + mt) % nk, (nt + mt + 1) % nk, ...: tiles that share
+    // weight rows (same nt) or token rows (same mt) reach each 128-byte k
+    // slice at different times, so one of them takes the L2 miss and the
+    // others hit (measured: GEMM2 17 % faster at the 16K prefill size).
+    // GEMM1 (16 stages at K = 2048) runs them in plain order: measured 2 %
+    // faster than the rotation at that size (the tiles of an XCD that share
+    // an operand then fetch each k slice at about the same time, while it is
+    // still in L2).  With scale groups (kG = 4) the groups of 4 stages are
+    // visited in an order rotated by rot/4 and the stages inside each group
+    // rotated by rot%4, so every group is still fetched whole at its first
+    // stage.  The accumulation order changes with it, deterministically per
+    // tile.
+    s.rot = kSwiglu ? 0 : uni((int)((ti.nt + (ti.m0 - s_row0[ti.e]) / kBM) % nk));
     return s;
   };
   // per-lane parts of the DMA offsets
