@@ -70,15 +70,6 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_any(
 // Codes: nearest of 0, .5, 1, 1.5, 2, 3, 4, 6, ties to the even code,
 // saturating at 6, sign kept; element 2i in the low nibble.
 
-__device__ __forceinline__ uint32_t e2m1_code(float x) {
-  const float a = fabsf(x);
-  // midpoints between neighbouring magnitudes; ">=" where the upper
-  // neighbour has the even code, ">" where the lower one has
-  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-  return c | (__float_as_uint(x) >> 31 << 3);
-}
-
 __device__ __forceinline__ uint32_t mxfp4_block32(const float (&v)[32], uint32_t (&q)[4]) {
   float amax = 0.0f;
 #pragma unroll
@@ -86,11 +77,20 @@ __device__ __forceinline__ uint32_t mxfp4_block32(const float (&v)[32], uint32_t
   const int field = static_cast<int>(__float_as_uint(amax) >> 23);
   const uint32_t sb = static_cast<uint32_t>(field > 2 ? field - 2 : 0);
   const float inv = e8m0_inverse(sb);   // 2^-s, exact scaling
+  // V_CVT_SCALEF32_PK_FP4_F32 (scale 1.0) on values already scaled by 2^-s
+  // exactly: two e2m1 codes per call, the first in the low nibble, into byte
+  // j of the word.  It rounds to nearest with ties to the even code,
+  // saturates at +-6 and keeps the sign of zero (a negative that rounds to 0
+  // is code 8): checked byte for byte against the format definition on every
+  // finite bf16 value and on random blocks.  (A compare-and-count encoder
+  // took 226 us for w13-shaped weights, this one 196 us.)
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) word |= e2m1_code(v[8 * w + j] * inv) << (4 * j);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[8 * w + 0] * inv, v[8 * w + 1] * inv, 1.0f, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[8 * w + 2] * inv, v[8 * w + 3] * inv, 1.0f, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[8 * w + 4] * inv, v[8 * w + 5] * inv, 1.0f, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[8 * w + 6] * inv, v[8 * w + 7] * inv, 1.0f, 3);
     q[w] = word;
   }
   return sb;
