@@ -57,7 +57,8 @@ def _all_finite_bf16():
     return bits[:n].reshape(-1, 64)
 
 
-@pytest.mark.parametrize("shape", [(1, 32), (7, 64), (33, 2048), (5, 4304), (3, 40), (130, 768), (2, 8)])
+@pytest.mark.parametrize("shape", [(1, 32), (7, 64), (33, 2048), (5, 4304), (3, 40), (130, 768), (2, 8),
+                                   (9, 4128), (4, 2080)])
 def test_mx_quantize_bitexact(shape):
     say(f"mx_quantize shape={shape}")
     x = _rand_bf16(shape, scale_spread=30)

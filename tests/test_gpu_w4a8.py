@@ -31,6 +31,18 @@ def test_mx_quantize_fp4_random_rows():
     _check_fp4_quant(bits, q, s)
 
 
+@pytest.mark.parametrize("shape", [(11, 4128), (6, 2080), (1, 32)])
+def test_mx_quantize_fp4_long_and_short_rows(shape):
+    """Rows longer than one pass of a wave's loads, with a ragged last pass."""
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal(shape).astype(np.float32) * np.exp2(rng.integers(-20, 20, (shape[0], 1))).astype(np.float32)
+    bits = to_bf16_bits(x)
+    say(f"mx_quantize_fp4 rows {shape}")
+    q, s = mx.mx_quantize_fp4(bf16_dev(bits))
+    torch.cuda.synchronize()
+    _check_fp4_quant(bits, q, s)
+
+
 def test_mx_quantize_fp4_every_bf16_value():
     """Every finite bf16 bit pattern, 32 per block in ascending order."""
     allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
