@@ -31,6 +31,15 @@
  * x * 2^-s rounded to nearest, ties to even, saturating at +-448, sign kept
  * (so -0 and negative values that round to zero give 0x80).
  *
+ * Finite inputs only.  Every bf16/fp32 input (x, bf16 weights, topk_w) must
+ * be finite: the pages fix no NaN or infinity convention for MX blocks and
+ * the library does not check (a device-side scan would cost a full read).
+ * What non-finite inputs produce is not part of the contract; with the
+ * current kernels a NaN drops out of its block's amax and encodes as -448
+ * times the block scale (code 0xFE), and an infinity sets its block's scale
+ * byte to 247 and flushes the block's other elements to zero.  No error is
+ * reported for either.
+ *
  * Tensors.  Every pointer is a DEVICE pointer unless stated; all tensors are
  * dense row-major.  bf16 is passed as its 16-bit pattern.  Sizes are int64_t.
  *   x            bf16   [T, K]

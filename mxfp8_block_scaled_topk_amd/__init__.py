@@ -13,6 +13,8 @@ type 0 = inclusive cumulative counts).
 """
 
 import ctypes
+import functools
+import inspect
 import os
 
 import torch
@@ -97,6 +99,26 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _stream_scoped(fn):
+    """Run ``fn`` with its ``stream`` argument (when given) as torch's current
+    stream.  Every tensor the binding allocates for the call (outputs left to
+    it, internal workspaces) then comes from that stream's pool of the caching
+    allocator: freed on return, such a workspace is reused only by later work
+    on the same stream, which runs after the kernels that used it.  Allocated
+    on another stream instead, it could be handed to work on that stream while
+    the kernels still read or write it."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kw):
+        s = sig.bind(*args, **kw).arguments.get("stream")
+        if s is None:
+            return fn(*args, **kw)
+        with torch.cuda.stream(s):
+            return fn(*args, **kw)
+    return wrapper
+
+
 # Argument checks.  The library receives raw pointers and sizes, so every
 # tensor is checked here for dtype, exact shape, contiguity and device before
 # the call: a tensor smaller than its sizes say would be read or written out
@@ -142,6 +164,7 @@ def _pairs(n):
     return -(-n // 64)
 
 
+@_stream_scoped
 def mx_quantize(x, q=None, s=None, stream=None):
     """MX-quantise the last dim of a bf16 tensor [..., Kd] (rows may be strided
     with unit inner stride).  Returns (q uint8 [..., Kd], s uint8 [..., ceil(Kd/64), 2])."""
@@ -169,6 +192,7 @@ def route_workspace_size(T, k, E):
     return int(load().moe_route_quant_workspace_size(T, k, E))
 
 
+@_stream_scoped
 def moe_route_quant(x, topk_ids, E, out=None, workspace=None, stream=None):
     """Routing with fused MX activation quant.
 
@@ -204,6 +228,8 @@ def moe_route_quant(x, topk_ids, E, out=None, workspace=None, stream=None):
     return xq, xs, sr, eri, gl
 
 
+
+@_stream_scoped
 def gmm_swiglu_mxquant(a, a_s, w13, w13_s, group_list, group_list_type=GROUP_COUNT, out=None,
                        h_debug=False, stream=None, _w4=False):
     """GEMM1 + SwiGLU + MX requant.  Returns (hq, hs) or (hq, hs, h) with h_debug."""
@@ -235,6 +261,7 @@ def gmm_swiglu_mxquant(a, a_s, w13, w13_s, group_list, group_list_type=GROUP_COU
     return (hq, hs, h) if h_debug else (hq, hs)
 
 
+@_stream_scoped
 def gmm_mx(a, a_s, w, w_s, group_list, group_list_type=GROUP_COUNT, out=None, stream=None, _w4=False):
     """Grouped MX GEMM, bf16 output [M, N]."""
     _need(a, torch.uint8, "a", 2); _need(w, torch.uint8, "w", 3)
@@ -260,6 +287,7 @@ def gmm_mx(a, a_s, w, w_s, group_list, group_list_type=GROUP_COUNT, out=None, st
     return out
 
 
+@_stream_scoped
 def moe_finalize(y, topk_w, expanded_row_idx, out=None, stream=None):
     """Weighted un-permute and sum: out [T, K] bf16."""
     _need(y, torch.bfloat16, "y", 2); _need(topk_w, torch.float32, "topk_w", 2)
@@ -290,6 +318,7 @@ def forward_workspace(T, K, I, E, k, device="cuda"):
     return torch.empty(max(forward_workspace_size(T, K, I, E, k), 256), dtype=torch.uint8, device=device)
 
 
+@_stream_scoped
 def moe_mxfp8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, workspace=None, stream=None,
                       _w4=False):
     """The whole layer.  x [T,K] bf16, topk_ids [T,k] i32, topk_w [T,k] f32,
@@ -350,6 +379,7 @@ def forward_intermediates(workspace, T, K, I, E, k):
     )
 
 
+@_stream_scoped
 def moe_router(x, gate, k, bias=None, renormalize=True, out=None, stream=None):
     """Top-k softmax router: x [T,K] bf16, gate [E,K] bf16, optional bias [E]
     fp32.  Returns (topk_ids [T,k] int32, topk_w [T,k] float32)."""
@@ -377,6 +407,7 @@ def linear_workspace_size(T, K):
     return int(load().mx_linear_workspace_size(T, K))
 
 
+@_stream_scoped
 def mx_linear(x, w, w_s, out=None, workspace=None, stream=None):
     """Dense MXFP8 linear: x [T,K] bf16, w [N,K] e4m3 bytes, w_s [N,K/64,2]
     e8m0 bytes (as mx_quantize makes them).  Returns y [T,N] bf16."""
@@ -403,6 +434,7 @@ def mx_linear(x, w, w_s, out=None, workspace=None, stream=None):
     return out
 
 
+@_stream_scoped
 def mx_quantize_fp4(x, q=None, s=None, stream=None):
     """MXFP4-quantise the last dim of a bf16 tensor [..., Kd] (Kd % 32 == 0).
     Returns (q uint8 [..., Kd/2] packed e2m1, s uint8 [..., ceil(Kd/64), 2])."""
@@ -428,6 +460,7 @@ def mx_quantize_fp4(x, q=None, s=None, stream=None):
     return q, s
 
 
+@_stream_scoped
 def gmm_swiglu_mxquant_w4a8(a, a_s, w13, w13_s, group_list, group_list_type=GROUP_COUNT, out=None,
                             h_debug=False, stream=None):
     """GEMM1 + SwiGLU + MX requant with MXFP4 weights: w13 [E, 2I, K/2] packed
@@ -435,11 +468,13 @@ def gmm_swiglu_mxquant_w4a8(a, a_s, w13, w13_s, group_list, group_list_type=GROU
     return gmm_swiglu_mxquant(a, a_s, w13, w13_s, group_list, group_list_type, out, h_debug, stream, _w4=True)
 
 
+@_stream_scoped
 def gmm_mx_w4a8(a, a_s, w, w_s, group_list, group_list_type=GROUP_COUNT, out=None, stream=None):
     """Grouped MX GEMM with MXFP4 weights (w [E, N, Kd/2] packed e2m1), bf16 [M, N]."""
     return gmm_mx(a, a_s, w, w_s, group_list, group_list_type, out, stream, _w4=True)
 
 
+@_stream_scoped
 def moe_w4a8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, workspace=None, stream=None):
     """The layer with MXFP4 expert weights: w13 [E,2I,K/2], w2 [E,K,I/2] packed e2m1."""
     return moe_mxfp8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out, workspace, stream, _w4=True)

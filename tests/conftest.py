@@ -4,13 +4,24 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-if ROOT not in sys.path:
-    sys.path.insert(0, ROOT)
+HERE = os.path.dirname(os.path.abspath(__file__))
+for _p in (HERE, ROOT):
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
 
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: large CPU oracle runs")
+    # the oracle's worker processes must be forked from a process that never
+    # touched the GPU: start their fork server before any test runs
+    import oracle_pool
+    oracle_pool.start_server()
+
+
+def pytest_unconfigure(config):
+    import oracle_pool
+    oracle_pool.shutdown()
 
 
 def read_golden(name):

@@ -143,3 +143,75 @@ def explain_hq_mismatches(hq, hs, hq_ref, h_ref, rtol=1e-3):
     sat = ((q & 0x7F) == 0x7E) & (np.sign(deq) * h >= np.abs(deq) - atol)
     ok |= sat
     return int(np.sum(hq != hq_ref)), int(np.sum(~ok))
+
+
+def explain_hq_mismatches_rows(hq, hs, hq_ref, h_ref, rows=8192):
+    """explain_hq_mismatches over row chunks (full-size matrices)."""
+    n_mis = n_bad = 0
+    for a in range(0, hq.shape[0], rows):
+        m, b = explain_hq_mismatches(hq[a:a + rows], hs[a:a + rows], hq_ref[a:a + rows], h_ref[a:a + rows])
+        n_mis += m
+        n_bad += b
+    return n_mis, n_bad
+
+
+def bf16_rows_rel_err_chunked(got_bits, ref_bits, rows=8192):
+    return np.concatenate([bf16_rows_rel_err(got_bits[a:a + rows], ref_bits[a:a + rows])
+                           for a in range(0, got_bits.shape[0], rows)] or [np.zeros(0)])
+
+
+def check_layer_every_row(d, out, inter, w13q, w13s, w2q, w2s, w_format, tol, e2e_tol):
+    """Every row of every stage of one layer call against the oracle.
+
+    * routing maps, group counts, xq and xs: bit-exact;
+    * GEMM1: the oracle's h from the oracle's own xq/xs; the GPU's hq/hs
+      bytes must equal the oracle's or be explained by the requant rule;
+    * GEMM2 on identical operands (the GPU's hq/hs): every row within
+      ``tol`` (per-row max relative error);
+    * finalize of the GPU's y: bit-exact, every token;
+    * end to end, every token: the oracle's chain (its own hq/hs into its
+      GEMM2; rows whose hq/hs bytes equal the GPU's give y exactly as on
+      identical operands, so only the others are recomputed), then its
+      finalize, within ``e2e_tol``.
+    Returns a dict of the measured figures."""
+    import oracle_pool
+    from oracle import moe_ref
+
+    cfg = d["cfg"]
+    K, I, k = cfg.K, cfg.I, cfg.k
+    counts, sr, eri = moe_ref.route_ref_fast(d["topk_ids"], cfg.E)
+    assert np.array_equal(inter["group_list"], counts)
+    assert np.array_equal(inter["sorted_row"], sr)
+    assert np.array_equal(inter["expanded_row_idx"], eri)
+    say(f"  {cfg.name}: oracle routing quant")
+    qt, st = oracle_pool.quantize_bf16(d["x"])
+    tok = sr.astype(np.int64) // k
+    xq, xs = qt[tok], st[tok]
+    assert np.array_equal(inter["xq"], xq)
+    assert np.array_equal(inter["xs"], xs)
+    M = xq.shape[0]
+
+    say(f"  {cfg.name}: oracle GEMM1 over {M} rows")
+    h_ref = oracle_pool.gemm1_h(xq, xs, w13q, w13s, counts, 1, I, w_format)
+    hq_ref, hs_ref = oracle_pool.quantize_f32(h_ref)
+    n_mis, n_bad = explain_hq_mismatches_rows(inter["hq"], inter["hs"], hq_ref, h_ref)
+    say(f"  {cfg.name}: hq/hs bytes differing from the oracle {n_mis} of {hq_ref.size}, unexplained {n_bad}")
+    assert n_bad == 0 and n_mis <= 0.01 * hq_ref.size
+
+    say(f"  {cfg.name}: oracle GEMM2 on the GPU's hq/hs")
+    y_same = oracle_pool.gemm2_y(inter["hq"], inter["hs"], w2q, w2s, counts, 1, w_format)
+    yerr = bf16_rows_rel_err_chunked(inter["y"], y_same)
+    assert np.array_equal(out, moe_ref.finalize_ref(inter["y"], d["topk_w"], inter["expanded_row_idx"]))
+
+    diff = np.nonzero((inter["hq"] != hq_ref).any(axis=1) |
+                      (inter["hs"].reshape(M, -1) != hs_ref.reshape(M, -1)).any(axis=1))[0]
+    y_ref = y_same.copy()
+    say(f"  {cfg.name}: oracle GEMM2 on its own hq/hs ({diff.size} rows differ)")
+    oracle_pool.gemm2_y(hq_ref, hs_ref, w2q, w2s, counts, 1, w_format, only_rows=diff, out=y_ref)
+    out_ref = moe_ref.finalize_ref(y_ref, d["topk_w"], eri)
+    e2e = bf16_rows_rel_err_chunked(out, out_ref)
+    say(f"  {cfg.name}: y max row rel err {yerr.max():.3g} over {M} rows (identical operands); "
+        f"{diff.size} rows with a requant difference; end-to-end out {e2e.max():.3g} over {out.shape[0]} tokens")
+    assert yerr.max() <= tol
+    assert e2e.max() <= e2e_tol
+    return dict(y_err=float(yerr.max()), e2e=float(e2e.max()), hq_mismatch=n_mis, rows_requant_diff=int(diff.size))

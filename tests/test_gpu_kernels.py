@@ -488,3 +488,56 @@ def test_finalize_skips_invalid_rows():
     eri2 = np.where(bad, 0, eri)
     ref = moe_ref.finalize_ref(y, w2.reshape(T, k), eri2)
     assert np.array_equal(bf16_host(out), ref)
+
+
+# --------------------------------------------------------------------------
+# guard bands around every output of the layer's entry points
+# --------------------------------------------------------------------------
+
+def _guarded(shape, dtype, fill):
+    n = int(np.prod(shape))
+    raw, t = guard_alloc(n, dtype, fill=fill)
+    return raw, t.view(shape), n * torch.empty((), dtype=dtype).element_size()
+
+
+def test_every_output_guard_bands():
+    """Each output buffer of moe_route_quant, gmm_swiglu_mxquant and
+    moe_finalize sits between 4 KB guard bands of a fill byte; after the calls
+    (on ragged shapes, several routing chunks, tail tiles) the bands are
+    intact and the outputs still match the oracle."""
+    T, K, k, E, I = 301, 512, 8, 64, 256
+    M = T * k
+    x = _rand_bf16((T, K), scale_spread=6)
+    ids = _distinct_ids(T, k, E)
+    outs = [_guarded((M, K), torch.uint8, 0x11), _guarded((M, K // 64, 2), torch.uint8, 0x22),
+            _guarded((M,), torch.int32, 0x33), _guarded((M,), torch.int32, 0x44), _guarded((E,), torch.int64, 0x55)]
+    say(f"guard bands: moe_route_quant T={T} K={K} k={k} E={E}")
+    mx.moe_route_quant(bf16_dev(x), i32_dev(ids), E, out=tuple(o[1] for o in outs))
+    torch.cuda.synchronize()
+    for (raw, t, nb), fill in zip(outs, (0x11, 0x22, 0x33, 0x44, 0x55)):
+        assert guards_intact(raw, nb, fill=fill)
+    rq, rs, rsr, reri, rc = moe_ref.route_quant_ref(x, ids, E)
+    xq, xs, sr, eri, gl = (o[1] for o in outs)
+    assert np.array_equal(host(xq), rq) and np.array_equal(host(xs), rs) and np.array_equal(host(gl), rc)
+    assert np.array_equal(host(sr), rsr) and np.array_equal(host(eri), reri)
+
+    w13 = (RNG.standard_normal((E * 2 * I, K)) * 0.05)
+    w13q, w13s = mx_ref.mx_quantize_ref(w13)
+    w13q, w13s = w13q.reshape(E, 2 * I, K), w13s.reshape(E, 2 * I, -1, 2)
+    hq_g, hs_g = _guarded((M, I), torch.uint8, 0x66), _guarded((M, I // 64, 2), torch.uint8, 0x77)
+    say(f"guard bands: gmm_swiglu_mxquant M={M} K={K} I={I} E={E}")
+    mx.gmm_swiglu_mxquant(xq, xs, u8_dev(w13q), u8_dev(w13s), gl, 1, out=(hq_g[1], hs_g[1]))
+    torch.cuda.synchronize()
+    assert guards_intact(hq_g[0], hq_g[2], fill=0x66) and guards_intact(hs_g[0], hs_g[2], fill=0x77)
+    rhq, rhs, rh = moe_ref.gmm_swiglu_mxquant_ref(rq, rs, w13q, w13s, rc, 1, I)
+    n_mis, n_bad = explain_hq_mismatches(host(hq_g[1]), host(hs_g[1]), rhq, rh)
+    assert n_bad == 0 and n_mis <= 0.01 * rhq.size
+
+    y = _rand_bf16((M, K), scale_spread=4)
+    w = RNG.random((T, k)).astype(np.float32)
+    out_g = _guarded((T, K), torch.bfloat16, 0x5A)
+    say(f"guard bands: moe_finalize T={T} K={K} k={k}")
+    mx.moe_finalize(bf16_dev(y), f32_dev(w), eri, out=out_g[1])
+    torch.cuda.synchronize()
+    assert guards_intact(out_g[0], out_g[2], fill=0x5A)
+    assert np.array_equal(bf16_host(out_g[1]), moe_ref.finalize_ref(y, w, reri))

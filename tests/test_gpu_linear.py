@@ -1,14 +1,16 @@
 """Dense MXFP8 linear (mx_linear) against the oracle: the oracle's MX
 quantisation of x followed by its MX GEMM with one group (the dense case the
-oracle pins against a direct float64 product).  Small shapes in full; the
-large one on sampled rows (rows are independent)."""
+oracle pins against a direct float64 product).  Every row, small shapes and
+the benchmark's 16384 x 4096 x 4096 shape."""
 
 import numpy as np
 import pytest
 import torch
 
 import mxfp8_block_scaled_topk_amd as mx
-from gpu_util import bf16_dev, bf16_host, bf16_rows_rel_err, say, u8_dev
+import oracle_pool
+from gpu_util import (bf16_dev, bf16_host, bf16_rows_rel_err, bf16_rows_rel_err_chunked, guard_alloc, guards_intact,
+                      say, u8_dev)
 from oracle import moe_ref, mx_ref
 from workloads import dense_linear_inputs, normal_bf16, rng_for
 
@@ -43,18 +45,20 @@ def test_linear_small(T, K, N, offline):
     assert err.max() <= TOL
 
 
-def test_linear_large_sampled():
-    """The benchmark's dense shape, sampled rows."""
+@pytest.mark.timeout(900)
+def test_linear_large_every_row():
+    """The benchmark's dense shape, every row, with guard bands around y."""
     T, K, N = 16384, 4096, 4096
     x, wq, ws = dense_linear_inputs(T, K, N)
-    say(f"mx_linear T={T} K={K} N={N} (sampled rows)")
-    y = mx.mx_linear(bf16_dev(x), u8_dev(wq), u8_dev(ws))
+    raw, y = guard_alloc(T * N, torch.bfloat16, fill=0x4D)
+    say(f"mx_linear T={T} K={K} N={N}")
+    mx.mx_linear(bf16_dev(x), u8_dev(wq), u8_dev(ws), out=y.view(T, N))
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(0).choice(T, 24, replace=False))
-    rows[0], rows[-1] = 0, T - 1
-    ref = oracle_rows(x, wq, ws, rows)
-    err = bf16_rows_rel_err(bf16_host(y)[rows], ref)
-    say(f"mx_linear large: max row rel err {err.max():.2e}")
+    assert guards_intact(raw, T * N * 2, fill=0x4D)
+    xq, xs = oracle_pool.quantize_bf16(x)
+    ref = oracle_pool.gemm2_y(xq, xs, wq[None], ws[None], np.array([T], np.int64), 1)
+    err = bf16_rows_rel_err_chunked(bf16_host(y.view(T, N)), ref)
+    say(f"mx_linear large: max row rel err {err.max():.2e} over {T} rows")
     assert err.max() <= TOL
 
 

@@ -131,3 +131,20 @@ def test_router_empty_and_feeds_the_layer():
     xq, xs, sr, eri, gl = mx.moe_route_quant(bf16_dev(xb), ids, cfg.E)
     torch.cuda.synchronize()
     assert int(host(gl).sum()) == cfg.T * cfg.k
+
+
+def test_router_guard_bands():
+    """topk_ids and topk_w sit between 4 KB guard bands (ragged token count,
+    a k that does not divide the wave); the bands stay intact."""
+    from gpu_util import guard_alloc, guards_intact
+    rng = np.random.default_rng(8)
+    T, K, E, k = 1001, 512, 96, 6
+    x = to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    gate = to_bf16_bits((rng.standard_normal((E, K)) * 0.02).astype(np.float32))
+    raw_i, ids = guard_alloc(T * k, torch.int32, fill=0x2D)
+    raw_w, w = guard_alloc(T * k, torch.float32, fill=0x4E)
+    say(f"moe_router guard bands T={T} K={K} E={E} k={k}")
+    mx.moe_router(bf16_dev(x), bf16_dev(gate), k, out=(ids.view(T, k), w.view(T, k)))
+    torch.cuda.synchronize()
+    assert guards_intact(raw_i, T * k * 4, fill=0x2D) and guards_intact(raw_w, T * k * 4, fill=0x4E)
+    check_router(host(ids.view(T, k)), host(w.view(T, k)), x, gate, None, k, True)

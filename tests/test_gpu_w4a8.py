@@ -70,8 +70,8 @@ def test_mx_quantize_fp4_strided_and_odd_scale_count():
 # grouped GEMMs with e2m1 weights
 # --------------------------------------------------------------------------
 
-from gpu_util import bf16_host, bf16_rows_rel_err, explain_hq_mismatches, f32_dev, i32_dev, i64_dev, \
-    row_rel_err, u8_dev  # noqa: E402
+from gpu_util import bf16_host, bf16_rows_rel_err, check_layer_every_row, explain_hq_mismatches, f32_dev, \
+    guard_alloc, guards_intact, i32_dev, i64_dev, row_rel_err, u8_dev  # noqa: E402
 from oracle import moe_ref  # noqa: E402
 from workloads import CONFIGS, custom_config, make_inputs, make_weights_w4a8  # noqa: E402
 
@@ -166,10 +166,27 @@ def test_gmm_swiglu_mxquant_w4a8_parity(name):
 # the layer with e2m1 weights
 # --------------------------------------------------------------------------
 
+def _run_w4a8(d, wdev, name):
+    cfg = d["cfg"]
+    T, K, I, E, k = cfg.T, cfg.K, cfg.I, cfg.E, cfg.k
+    need = mx.forward_workspace_size(T, K, I, E, k)
+    raw_ws, ws = guard_alloc(need, torch.uint8, fill=0x3C)
+    raw_out, out = guard_alloc(T * K, torch.bfloat16, fill=0x6B)
+    say(f"moe_w4a8_forward {name} T={T} K={K} I={I} E={E} k={k}")
+    mx.moe_w4a8_forward(bf16_dev(d["x"]), i32_dev(d["topk_ids"]), f32_dev(d["topk_w"]), *wdev,
+                        out=out.view(T, K), workspace=ws)
+    torch.cuda.synchronize()
+    assert guards_intact(raw_ws, need, fill=0x3C) and guards_intact(raw_out, T * K * 2, fill=0x6B)
+    iv = mx.forward_intermediates(ws, T, K, I, E, k)
+    inter = {n: host(v) for n, v in iv.items() if n != "y"}
+    inter["y"] = bf16_host(iv["y"])
+    return bf16_host(out.view(T, K)), inter
+
+
 @pytest.mark.parametrize("shape", [("tiny", None), ("several-tiles", (300, 512, 256, 12, 4))])
 def test_w4a8_forward_small(shape):
     """bf16 weights quantised to MXFP4 by the library (checked byte for byte),
-    then the layer against the oracle in full."""
+    then every stage of the layer against the oracle on every row."""
     name, dims = shape
     cfg = CONFIGS["tiny"] if dims is None else custom_config(name, *dims)
     d = make_inputs(cfg)
@@ -179,37 +196,23 @@ def test_w4a8_forward_small(shape):
     torch.cuda.synchronize()
     r13q, r13s = mx_ref.mxfp4_quantize_ref(mx_ref.bf16_to_f64(d["w13"].reshape(-1, K)))
     r2q, r2s = mx_ref.mxfp4_quantize_ref(mx_ref.bf16_to_f64(d["w2"].reshape(-1, I)))
-    assert np.array_equal(host(w13q).reshape(r13q.shape), r13q) and np.array_equal(host(w2s).reshape(r2s.shape), r2s)
-    say(f"moe_w4a8_forward {cfg.name} T={T} K={K} I={I} E={E} k={k}")
-    out = mx.moe_w4a8_forward(bf16_dev(d["x"]), i32_dev(d["topk_ids"]), f32_dev(d["topk_w"]), w13q, w13s, w2q, w2s)
-    torch.cuda.synchronize()
-    ref = moe_ref.moe_forward_ref(d["x"], d["topk_ids"], d["topk_w"], r13q.reshape(E, 2 * I, K // 2),
-                                  r13s.reshape(E, 2 * I, -1, 2), r2q.reshape(E, K, I // 2), r2s.reshape(E, K, -1, 2),
-                                  "e2m1")
-    e2e = bf16_rows_rel_err(bf16_host(out), ref["out"])
-    say(f"  end-to-end out max row rel err {e2e.max():.3g}")
-    assert e2e.max() <= E2E_TOL
+    assert np.array_equal(host(w13q).reshape(r13q.shape), r13q) and np.array_equal(host(w13s).reshape(r13s.shape), r13s)
+    assert np.array_equal(host(w2q).reshape(r2q.shape), r2q) and np.array_equal(host(w2s).reshape(r2s.shape), r2s)
+    out, inter = _run_w4a8(d, [w13q, w13s, w2q, w2s], cfg.name)
+    check_layer_every_row(d, out, inter, r13q.reshape(E, 2 * I, K // 2), r13s.reshape(E, 2 * I, -1, 2),
+                          r2q.reshape(E, K, I // 2), r2s.reshape(E, K, -1, 2), "e2m1", TOL, E2E_TOL)
 
 
-def test_w4a8_forward_prefill_sampled():
+@pytest.mark.timeout(900)
+def test_w4a8_forward_prefill_every_row():
     """The 16K prefill layer with checkpoint-style MXFP4 weights, in the
-    benchmark's launch configuration; sampled tokens through the oracle's
-    per-token path."""
+    benchmark's launch configuration: every row of every stage against the
+    oracle (GEMM2 on identical operands at 2e-2, finalize bit-exact)."""
     cfg = CONFIGS["prefill"]
     d = make_inputs(cfg, weights=False)
     wts = make_weights_w4a8(cfg)
-    T, K, I, E, k = cfg.T, cfg.K, cfg.I, cfg.E, cfg.k
     wdev = [u8_dev(wts[n]) for n in ("w13q4", "w13s4", "w2q4", "w2s4")]
-    ws = mx.forward_workspace(T, K, I, E, k)
-    say(f"moe_w4a8_forward prefill T={T} K={K} I={I} E={E} k={k}")
-    out = mx.moe_w4a8_forward(bf16_dev(d["x"]), i32_dev(d["topk_ids"]), f32_dev(d["topk_w"]), *wdev, workspace=ws)
-    torch.cuda.synchronize()
-    out = bf16_host(out)
-    tokens = np.sort(np.random.default_rng(5).choice(T, 12, replace=False))
-    worst = 0.0
-    for t in tokens:
-        o_ref, _ = moe_ref.moe_token_ref(d["x"][t], d["topk_ids"][t], d["topk_w"][t], wts["w13q4"], wts["w13s4"],
-                                         wts["w2q4"], wts["w2s4"], "e2m1")
-        worst = max(worst, bf16_rows_rel_err(out[t:t + 1], o_ref.reshape(1, -1))[0])
-    say(f"  prefill sampled {len(tokens)} tokens: end-to-end out max row rel err {worst:.3g}")
-    assert worst <= E2E_TOL
+    out, inter = _run_w4a8(d, wdev, "prefill")
+    del wdev
+    check_layer_every_row(d, out, inter, wts["w13q4"], wts["w13s4"], wts["w2q4"], wts["w2s4"], "e2m1", TOL,
+                          E2E_TOL)
