@@ -12,6 +12,8 @@
  *   moe_finalize        weighted un-permute and sum of the top-k outputs
  *   moe_mxfp8_forward   the four steps above on one stream
  *   mx_quantize         stand-alone MX quantiser (weights at load time)
+ *   moe_route_quant_noalloc
+ *                       moe_route_quant without a workspace (allocates nothing)
  *   moe_router          top-k softmax router over a bf16 gate (upstream of
  *                       the layer: produces the ids and weights it takes)
  *   mx_linear           dense MXFP8 linear layer (activation quant + MX GEMM)
@@ -146,6 +148,28 @@ int moe_route_quant(const void* x_bf16, const int32_t* topk_ids,
                     void* xq_u8, void* xs_u8, int32_t* sorted_row,
                     int32_t* expanded_row_idx, int64_t* group_list,
                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_quant for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, outputs and results as moe_route_quant minus the workspace:
+ * the routing scratch (per-chunk expert counts and the experts' totals) is
+ * a 4 MiB device array inside the library, one per GPU, held until the
+ * process ends.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the caller still passes every input and
+ * output.  Sizes whose scratch, moe_route_quant_workspace_size(T, k, E),
+ * exceeds 4 MiB (4,194,304 bytes) are rejected with MX_ERR_UNSUPPORTED
+ * before anything is enqueued (e.g. E = 128, k = 8: up to 262,112 tokens).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and must not be
+ * issued; calls ordered on one stream are safe.  The array needs no
+ * clearing: each call writes every element it reads before reading it.
+ */
+int moe_route_quant_noalloc(const void* x_bf16, const int32_t* topk_ids,
+                            int64_t T, int64_t K, int64_t k, int64_t E,
+                            void* xq_u8, void* xs_u8, int32_t* sorted_row,
+                            int32_t* expanded_row_idx, int64_t* group_list,
+                            void* stream);
 
 /*
  * Grouped GEMM1 with SwiGLU and MX requant fused ("Quantization on Ascend",

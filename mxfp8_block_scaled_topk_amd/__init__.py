@@ -23,7 +23,7 @@ __all__ = [
     "MxError", "lib_path", "load", "mx_quantize", "moe_route_quant", "gmm_swiglu_mxquant",
     "gmm_mx", "moe_finalize", "moe_mxfp8_forward", "forward_workspace", "forward_intermediates",
     "route_workspace_size", "forward_workspace_size", "last_error", "moe_router", "mx_linear",
-    "linear_workspace_size", "mx_quantize_fp4", "gmm_mx_w4a8", "gmm_swiglu_mxquant_w4a8", "moe_w4a8_forward",
+    "linear_workspace_size", "mx_quantize_fp4", "moe_route_quant_noalloc", "gmm_mx_w4a8", "gmm_swiglu_mxquant_w4a8", "moe_w4a8_forward",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +59,7 @@ def load():
         "mx_quantize_fp4": (I32, [P, I64, I64, I64, P, P, P]),
         "moe_route_quant_workspace_size": (SZ, [I64, I64, I64]),
         "moe_route_quant": (I32, [P, P, I64, I64, I64, I64, P, P, P, P, P, P, SZ, P]),
+        "moe_route_quant_noalloc": (I32, [P, P, I64, I64, I64, I64, P, P, P, P, P, P]),
         "gmm_swiglu_mxquant": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P, P, P]),
         "gmm_mx": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]),
         "gmm_mx_w4a8": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]),
@@ -227,6 +228,37 @@ def moe_route_quant(x, topk_ids, E, out=None, workspace=None, stream=None):
     _check(rc, "moe_route_quant")
     return xq, xs, sr, eri, gl
 
+
+@_stream_scoped
+def moe_route_quant_noalloc(x, topk_ids, E, out=None, stream=None):
+    """moe_route_quant with the routing scratch held by the library (no
+    workspace; the C call allocates nothing).  The caller may pass the
+    outputs preallocated in ``out`` (then this call allocates nothing either).
+    Returns (xq, xs, sorted_row, expanded_row_idx, group_list)."""
+    _need(x, torch.bfloat16, "x", 2); _need(topk_ids, torch.int32, "topk_ids", 2)
+    T, K = x.shape
+    k = topk_ids.shape[1]
+    M = T * k
+    dev = x.device
+    _need_shape(x, (T, K), "x", torch.bfloat16, dev)
+    _need_shape(topk_ids, (T, k), "topk_ids", torch.int32, dev)
+    if out is None:
+        out = (torch.empty((M, K), dtype=torch.uint8, device=dev),
+               torch.empty((M, _pairs(K), 2), dtype=torch.uint8, device=dev),
+               torch.empty(M, dtype=torch.int32, device=dev),
+               torch.empty(M, dtype=torch.int32, device=dev),
+               torch.empty(E, dtype=torch.int64, device=dev))
+    xq, xs, sr, eri, gl = out
+    _need_shape(xq, (M, K), "xq", torch.uint8, dev)
+    _need_shape(xs, (M, _pairs(K), 2), "xs", torch.uint8, dev)
+    _need_shape(sr, (M,), "sorted_row", torch.int32, dev)
+    _need_shape(eri, (M,), "expanded_row_idx", torch.int32, dev)
+    _need_shape(gl, (E,), "group_list", torch.int64, dev)
+    _need_gpu(x, "x")
+    rc = load().moe_route_quant_noalloc(_ptr(x), _ptr(topk_ids), T, K, k, E, _ptr(xq), _ptr(xs), _ptr(sr), _ptr(eri),
+                                        _ptr(gl), _stream(stream))
+    _check(rc, "moe_route_quant_noalloc")
+    return xq, xs, sr, eri, gl
 
 
 @_stream_scoped

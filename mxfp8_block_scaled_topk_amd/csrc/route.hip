@@ -32,6 +32,7 @@
 // The order inside an expert is the flat index order, so the permutation is
 // deterministic and equals a stable sort by expert.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -325,4 +326,76 @@ extern "C" int moe_route_quant(const void* x_bf16, const int32_t* topk_ids, int6
   return launch_route_quant(static_cast<const uint16_t*>(x_bf16), topk_ids, T, K, k, E,
                             static_cast<uint8_t*>(xq_u8), static_cast<uint8_t*>(xs_u8), sorted_row,
                             expanded_row_idx, group_list, workspace, as_stream(stream));
+}
+
+// ---------------------------------------------------------------------------
+// moe_route_quant_noalloc: the same routing for callers that cannot allocate
+// (code under graph capture, tight serving loops).  The only scratch the
+// routing kernels use -- per-chunk expert counts, scanned in place, and the
+// experts' totals -- lives in this file-scope device array instead of a
+// caller workspace.  Every element the kernels read is first written by the
+// same call (the histogram writes every chunk's count of every expert, the
+// scan every total), so nothing needs clearing between calls; calls that
+// overlap on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+
+namespace mxmoe {
+constexpr size_t kRouteScratchBytes = (size_t)4 << 20;
+}  // namespace mxmoe
+
+// The routing scratch of moe_route_quant_noalloc: each GPU the library runs
+// on holds its own copy until the process ends.
+static __device__ __align__(256) uint8_t scratch[mxmoe::kRouteScratchBytes];
+
+namespace mxmoe {
+namespace {
+
+std::mutex g_scratch_mutex;
+void* g_scratch_dev[64] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the array's name in host code is only a handle for the lookup).
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MX_ERR_HIP, "moe_route_quant_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MX_ERR_UNSUPPORTED, "moe_route_quant_noalloc: device %d >= 64", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MX_ERR_HIP, "moe_route_quant_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MX_OK;
+}
+
+}  // namespace
+}  // namespace mxmoe
+
+extern "C" int moe_route_quant_noalloc(const void* x_bf16, const int32_t* topk_ids, int64_t T, int64_t K,
+                                       int64_t k, int64_t E, void* xq_u8, void* xs_u8, int32_t* sorted_row,
+                                       int32_t* expanded_row_idx, int64_t* group_list, void* stream) {
+  using namespace mxmoe;
+  int rc = check_route_args(T, K, k, E);
+  if (rc) return rc;
+  if (!group_list) return fail(MX_ERR_INVALID_ARG, "moe_route_quant_noalloc: null pointer");
+  if (T > 0 && (!x_bf16 || !topk_ids || !xq_u8 || !xs_u8 || !sorted_row || !expanded_row_idx))
+    return fail(MX_ERR_INVALID_ARG, "moe_route_quant_noalloc: null pointer");
+  const size_t need = route_workspace_bytes(T, k, E);
+  if (need > kRouteScratchBytes)
+    return fail(MX_ERR_UNSUPPORTED,
+                "moe_route_quant_noalloc: T=%lld k=%lld E=%lld needs %zu bytes of routing scratch, more than the "
+                "%zu the library holds; use moe_route_quant with a workspace",
+                (long long)T, (long long)k, (long long)E, need, kRouteScratchBytes);
+  if (reinterpret_cast<uintptr_t>(x_bf16) % 16 || reinterpret_cast<uintptr_t>(xq_u8) % 16)
+    return fail(MX_ERR_UNSUPPORTED, "moe_route_quant_noalloc: x and xq must be 16-byte aligned");
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  return launch_route_quant(static_cast<const uint16_t*>(x_bf16), topk_ids, T, K, k, E,
+                            static_cast<uint8_t*>(xq_u8), static_cast<uint8_t*>(xs_u8), sorted_row,
+                            expanded_row_idx, group_list, ws, as_stream(stream));
 }

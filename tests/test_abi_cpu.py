@@ -76,6 +76,25 @@ def test_route_validation(lib):
     assert f(None, FAKE, 64, 256, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
 
 
+
+def test_route_noalloc_validation(lib):
+    """The allocation-free routing entry point checks the same arguments and
+    rejects sizes whose routing scratch exceeds the 4 MiB it holds, all on
+    the host (no GPU is touched)."""
+    f = lib.moe_route_quant_noalloc
+    args = lambda T, K, k, E: f(FAKE, FAKE, T, K, k, E, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert args(64, 256, 9, 8) == INVALID
+    assert args(64, 100, 2, 8) == UNSUPPORTED
+    assert args(64, 256, 2, 2048) == UNSUPPORTED
+    assert f(None, FAKE, 64, 256, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 64, 256, 2, 8, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
+    # E = 1024, top-8: 1024 routing chunks (32768 tokens) need 4 MiB of counts plus the totals
+    assert mx.route_workspace_size(32768, 8, 1024) > 4 << 20
+    assert mx.route_workspace_size(32768 - 32, 8, 1024) <= 4 << 20
+    assert args(32768, 256, 8, 1024) == UNSUPPORTED
+    assert "routing scratch" in mx.last_error()
+    assert mx.route_workspace_size(262112, 8, 128) <= 4 << 20 < mx.route_workspace_size(262113, 8, 128)
+
 def test_gmm_validation(lib):
     g = lib.gmm_mx
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, 256, 128, 4, FAKE, None) == INVALID   # bad type
