@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/mxmoe.h"
 
 namespace mxmoe {
@@ -24,6 +26,18 @@ int check_launch(const char* what);
 int num_cus();
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Largest value any size argument may take (MX_ERR_UNSUPPORTED above it).
+// With every dimension at most 2^31 - 1, the host's products of two sizes
+// stay far inside int64_t, so no size arithmetic can overflow.
+constexpr int64_t kMaxDim = ((int64_t)1 << 31) - 1;
+
+// True when every value lies in [0, kMaxDim].
+inline bool dims_in_range(std::initializer_list<int64_t> dims) {
+  for (int64_t d : dims)
+    if (d < 0 || d > kMaxDim) return false;
+  return true;
+}
 
 constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -104,6 +104,7 @@ int check_finalize_args(int64_t T, int64_t K, int64_t k, int64_t M) {
   if (T < 0 || K <= 0 || k <= 0 || M < 0)
     return fail(MX_ERR_INVALID_ARG, "moe_finalize: bad sizes T=%lld K=%lld k=%lld M=%lld", (long long)T,
                 (long long)K, (long long)k, (long long)M);
+  if (!dims_in_range({T, K, k})) return fail(MX_ERR_UNSUPPORTED, "moe_finalize: T, K or k above 2^31 - 1");
   if (K % 8 != 0) return fail(MX_ERR_UNSUPPORTED, "moe_finalize: K=%lld is not a multiple of 8", (long long)K);
   if (M >= (int64_t)1 << 31) return fail(MX_ERR_UNSUPPORTED, "moe_finalize: M >= 2^31");
   return MX_OK;

@@ -58,6 +58,7 @@ int check_forward_args(int64_t T, int64_t K, int64_t I, int64_t E, int64_t k) {
   int rc = check_route_args(T, K, k, E);
   if (rc) return rc;
   if (I <= 0) return fail(MX_ERR_INVALID_ARG, "moe_mxfp8_forward: bad I=%lld", (long long)I);
+  if (!dims_in_range({I})) return fail(MX_ERR_UNSUPPORTED, "moe_mxfp8_forward: I above 2^31 - 1");
   if (K % 256 != 0 || I % 128 != 0)
     return fail(MX_ERR_UNSUPPORTED, "moe_mxfp8_forward: K=%lld must be a multiple of 256 and I=%lld of 128",
                 (long long)K, (long long)I);
@@ -69,7 +70,8 @@ int check_forward_args(int64_t T, int64_t K, int64_t I, int64_t E, int64_t k) {
 }  // namespace mxmoe
 
 extern "C" size_t moe_mxfp8_forward_workspace_size(int64_t T, int64_t K, int64_t I, int64_t E, int64_t k) {
-  if (T < 0 || K <= 0 || I <= 0 || E <= 0 || k <= 0) return 0;
+  // 0 for sizes the forward rejects
+  if (mxmoe::check_forward_args(T, K, I, E, k) != MX_OK) return 0;
   return mxmoe::layout(T, K, I, E, k).total;
 }
 

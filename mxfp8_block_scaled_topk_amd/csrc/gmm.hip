@@ -72,6 +72,7 @@ constexpr int BN = 256;  // weight rows per tile
 constexpr int BK = 128;  // K bytes per stage
 constexpr int kThreads = 512;
 constexpr int kMaxE = 1024;
+constexpr int64_t kMaxKd = (int64_t)1 << 20;   // reduction size limit (32-bit DMA offsets)
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -869,6 +870,9 @@ int check_gmm_common(const char* name, int gl_type, int64_t M, int64_t Kd, int64
                 gl_type);
   if (Kd % BK != 0) return fail(MX_ERR_UNSUPPORTED, "%s: reduction size %lld is not a multiple of %d", name,
                                 (long long)Kd, BK);
+  // the DMA addresses a tile's 256 rows with 32-bit byte offsets
+  if (Kd > kMaxKd) return fail(MX_ERR_UNSUPPORTED, "%s: reduction size %lld > %lld", name, (long long)Kd,
+                               (long long)kMaxKd);
   if (E > kMaxE) return fail(MX_ERR_UNSUPPORTED, "%s: E=%lld > %d", name, (long long)E, kMaxE);
   if (M >= (int64_t)1 << 31) return fail(MX_ERR_UNSUPPORTED, "%s: M >= 2^31", name);
   return MX_OK;
@@ -906,6 +910,7 @@ int gmm_mx_entry(const char* name, bool w4, const void* a_u8, const void* a_s, c
   int rc = check_gmm_common(name, group_list_type, M, Kd, E);
   if (rc) return rc;
   if (N <= 0) return fail(MX_ERR_INVALID_ARG, "%s: bad N=%lld", name, (long long)N);
+  if (!dims_in_range({N})) return fail(MX_ERR_UNSUPPORTED, "%s: N above 2^31 - 1", name);
   if (N % BN != 0) return fail(MX_ERR_UNSUPPORTED, "%s: N=%lld is not a multiple of %d", name, (long long)N, BN);
   if (!group_list || (M > 0 && (!a_u8 || !a_s || !w_u8 || !w_s || !y_bf16)))
     return fail(MX_ERR_INVALID_ARG, "%s: null pointer", name);
@@ -926,6 +931,7 @@ int gmm_swiglu_entry(const char* name, bool w4, const void* a_u8, const void* a_
   int rc = check_gmm_common(name, group_list_type, M, K, E);
   if (rc) return rc;
   if (I <= 0) return fail(MX_ERR_INVALID_ARG, "%s: bad I=%lld", name, (long long)I);
+  if (!dims_in_range({I})) return fail(MX_ERR_UNSUPPORTED, "%s: I above 2^31 - 1", name);
   if (I % (BN / 2) != 0)
     return fail(MX_ERR_UNSUPPORTED, "%s: I=%lld is not a multiple of %d", name, (long long)I, BN / 2);
   if (!group_list || (M > 0 && (!a_u8 || !a_s || !w13_u8 || !w13_s || !hq_u8 || !hs_u8)))

@@ -37,7 +37,8 @@ LinearLayout linear_layout(int64_t T, int64_t K) {
 }  // namespace mxmoe
 
 extern "C" size_t mx_linear_workspace_size(int64_t T, int64_t K) {
-  if (T < 0 || K <= 0) return 0;
+  // 0 for sizes mx_linear rejects
+  if (mxmoe::check_gmm_common("mx_linear", 1, T, K, 1) != MX_OK) return 0;
   return mxmoe::linear_layout(T, K).total;
 }
 
@@ -47,6 +48,7 @@ extern "C" int mx_linear(const void* x_bf16, const void* w_u8, const void* w_s, 
   int rc = check_gmm_common("mx_linear", 1, T, K, 1);
   if (rc) return rc;
   if (N <= 0) return fail(MX_ERR_INVALID_ARG, "mx_linear: bad N=%lld", (long long)N);
+  if (!dims_in_range({N})) return fail(MX_ERR_UNSUPPORTED, "mx_linear: N above 2^31 - 1");
   if (N % 256 != 0) return fail(MX_ERR_UNSUPPORTED, "mx_linear: N=%lld is not a multiple of 256", (long long)N);
   if (T > 0 && (!x_bf16 || !w_u8 || !w_s || !y_bf16 || !workspace))
     return fail(MX_ERR_INVALID_ARG, "mx_linear: null pointer");

@@ -176,6 +176,7 @@ extern "C" int mx_quantize(const void* x_bf16, int64_t rows, int64_t kd, int64_t
   if (rows < 0 || kd <= 0 || ld < kd)
     return fail(MX_ERR_INVALID_ARG, "mx_quantize: bad sizes rows=%lld kd=%lld ld=%lld",
                 (long long)rows, (long long)kd, (long long)ld);
+  if (!dims_in_range({rows, ld})) return fail(MX_ERR_UNSUPPORTED, "mx_quantize: rows or ld above 2^31 - 1");
   return launch_mx_quantize(static_cast<const uint16_t*>(x_bf16), rows, kd, ld,
                             static_cast<uint8_t*>(q_u8), static_cast<uint8_t*>(s_u8),
                             as_stream(stream));
@@ -188,6 +189,7 @@ extern "C" int mx_quantize_fp4(const void* x_bf16, int64_t rows, int64_t kd, int
   if (rows < 0 || kd <= 0 || ld < kd)
     return fail(MX_ERR_INVALID_ARG, "mx_quantize_fp4: bad sizes rows=%lld kd=%lld ld=%lld",
                 (long long)rows, (long long)kd, (long long)ld);
+  if (!dims_in_range({rows, ld})) return fail(MX_ERR_UNSUPPORTED, "mx_quantize_fp4: rows or ld above 2^31 - 1");
   if (kd % 32 != 0)
     return fail(MX_ERR_UNSUPPORTED, "mx_quantize_fp4: kd=%lld is not a multiple of 32", (long long)kd);
   return launch_mx_quantize_fp4(static_cast<const uint16_t*>(x_bf16), rows, kd, ld,

@@ -262,6 +262,7 @@ int check_route_args(int64_t T, int64_t K, int64_t k, int64_t E) {
     return fail(MX_ERR_INVALID_ARG, "moe_route_quant: bad sizes T=%lld K=%lld k=%lld E=%lld",
                 (long long)T, (long long)K, (long long)k, (long long)E);
   if (k > E) return fail(MX_ERR_INVALID_ARG, "moe_route_quant: k=%lld > E=%lld", (long long)k, (long long)E);
+  if (!dims_in_range({T, K})) return fail(MX_ERR_UNSUPPORTED, "moe_route_quant: T or K above 2^31 - 1");
   if (K % 32 != 0) return fail(MX_ERR_UNSUPPORTED, "moe_route_quant: K=%lld is not a multiple of 32", (long long)K);
   if (k > kThreads) return fail(MX_ERR_UNSUPPORTED, "moe_route_quant: k=%lld > %d", (long long)k, kThreads);
   if (E > kMaxE) return fail(MX_ERR_UNSUPPORTED, "moe_route_quant: E=%lld > %d", (long long)E, kMaxE);
@@ -304,7 +305,8 @@ int launch_route_quant(const uint16_t* x, const int32_t* ids, int64_t T, int64_t
 }  // namespace mxmoe
 
 extern "C" size_t moe_route_quant_workspace_size(int64_t T, int64_t k, int64_t E) {
-  if (T < 0 || k <= 0 || E <= 0) return 0;
+  // 0 for sizes the routing rejects (the workspace of a call that fails)
+  if (mxmoe::check_route_args(T, 32, k, E) != MX_OK) return 0;
   return mxmoe::route_workspace_bytes(T, k, E);
 }
 

@@ -307,6 +307,7 @@ extern "C" int moe_router(const void* x_bf16, const void* gate_bf16, const float
     return fail(MX_ERR_INVALID_ARG, "moe_router: bad sizes T=%lld K=%lld E=%lld k=%lld", (long long)T,
                 (long long)K, (long long)E, (long long)k);
   if (k > E) return fail(MX_ERR_INVALID_ARG, "moe_router: k=%lld > E=%lld", (long long)k, (long long)E);
+  if (!dims_in_range({T, K})) return fail(MX_ERR_UNSUPPORTED, "moe_router: T or K above 2^31 - 1");
   if (E > kMaxE) return fail(MX_ERR_UNSUPPORTED, "moe_router: E=%lld > %d", (long long)E, kMaxE);
   if (K % kCK != 0) return fail(MX_ERR_UNSUPPORTED, "moe_router: K=%lld is not a multiple of %d", (long long)K, kCK);
   if (T > 0 && (!x_bf16 || !gate_bf16 || !topk_ids || !topk_w))
