@@ -73,8 +73,10 @@
  * it counts toward no expert, so sum(group_list) < T*k tells the caller), and
  * group lists are clamped to [0, M] rows.
  *
- * GPU shape limits (MX_ERR_UNSUPPORTED otherwise): GEMM reduction dims (K of
- * GEMM1, I of GEMM2) multiples of 128; GEMM2 output dim N a multiple of 256;
+ * GPU shape limits (MX_ERR_UNSUPPORTED otherwise): every size argument at
+ * most 2^31 - 1, and M = T*k below 2^31; GEMM reduction dims (K of GEMM1,
+ * I of GEMM2) multiples of 128 and at most 2^20; GEMM2 output dim N a
+ * multiple of 256;
  * GEMM1 intermediate size I a multiple of 128 (so the forward needs K % 256
  * == 0 and I % 128 == 0); routing needs K % 32 == 0, 1 <= k <= 256 and
  * E <= 1024; mx_quantize takes any Kd >= 1.
