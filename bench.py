@@ -89,27 +89,78 @@ def algorithmic(cfg, counts):
     }
 
 
-def cpu_baseline(d, tokens=2048):
-    """The oracle, as it stands, on the first `tokens` tokens of the workload."""
-    from oracle import moe_ref
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
-    t0 = time.perf_counter()
-    moe_ref.moe_forward_ref(d["x"][:tokens], d["topk_ids"][:tokens], d["topk_w"][:tokens], d["w13q"], d["w13s"],
-                            d["w2q"], d["w2s"])
-    dt = time.perf_counter() - t0
-    cpu = "unknown"
+def _host_cpu():
+    """The host CPU as /proc/cpuinfo names it (model name, family, model,
+    stepping) and the number of logical CPUs this process may use."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
-            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
-    except (OSError, StopIteration):
+            for line in f:
+                if ":" not in line:
+                    if info:
+                        break
+                    continue
+                k, v = (t.strip() for t in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping", "vendor_id") and k not in info:
+                    info[k] = v
+    except OSError:
         pass
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "cpu": cpu, "kind": "oracle",
-            "sample": f"first {tokens} of {CFG.T} tokens of the same workload (all {CFG.E} experts), "
-                      f"full oracle layer, {dt:.1f} s"}
+    name = info.get("model name", "unknown")
+    if "cpu family" in info:
+        name += f" (vendor {info.get('vendor_id', '?')}, family {info['cpu family']}, model {info.get('model', '?')}, " \
+                f"stepping {info.get('stepping', '?')})"
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count()
+    return name, usable, os.cpu_count()
+
+
+def cpu_baseline(d, gpu_out=None):
+    """The oracle, as it stands, on the whole 16K prefill layer: its stage
+    functions in the layer's order (routing with the MX activation quant;
+    GEMM1 + SwiGLU + requant; GEMM2; finalize), each stage timed on its own.
+    The oracle's arithmetic is row-, token- and expert-wise, so each stage
+    runs its oracle routine on chunks of rows (the GEMMs expert by expert)
+    over a pool of single-threaded worker processes (tests/oracle_pool.py:
+    the same bytes as the oracle's whole-matrix routines, pinned by a CPU
+    test); the routing maps and the gathers run in this process."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle_pool
+    from oracle import moe_ref, mx_ref
+    cfg = d["cfg"]
+    stages = {}
+    t_all = time.perf_counter()
+    t0 = time.perf_counter()
+    xq, xs, _, eri, counts = oracle_pool.route_quant(d["x"], d["topk_ids"], cfg.E)
+    stages["route_quant"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    h = oracle_pool.gemm1_h(xq, xs, d["w13q"], d["w13s"], counts, 1, cfg.I)
+    hq, hs = oracle_pool.quantize_f32(h)
+    stages["gemm1_swiglu_requant"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    y = oracle_pool.gemm2_y(hq, hs, d["w2q"], d["w2s"], counts, 1)
+    stages["gemm2"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    out = oracle_pool.finalize(y, d["topk_w"], eri)
+    stages["finalize"] = time.perf_counter() - t0
+    total = sum(stages.values())
+    wall = time.perf_counter() - t_all
+    workers = oracle_pool.n_workers()
+    oracle_pool.shutdown()
+    cpu, usable, logical = _host_cpu()
+    rec = {"value": round(cfg.T / total, 1), "unit": "tokens/s", "cores": workers, "cpu": cpu,
+           "host_logical_cpus": logical, "usable_cpus": usable, "kind": "oracle",
+           "stage_s": {n: round(v, 2) for n, v in stages.items()}, "total_s": round(total, 2),
+           "sample": f"the whole layer: all {cfg.T} tokens, all {cfg.E} experts; each stage's oracle routine "
+                     f"on row chunks (the GEMMs expert by expert) over {workers} single-threaded worker "
+                     f"processes ({wall:.1f} s wall)"}
+    if gpu_out is not None:
+        got = mx_ref.bf16_to_f64(gpu_out)
+        ref = mx_ref.bf16_to_f64(out)
+        den = np.abs(ref).max(axis=1)
+        rec["gpu_out_max_row_rel_err"] = float((np.abs(got - ref).max(axis=1) / np.where(den > 0, den, 1)).max())
+    return rec
 
 
 def _dev_inputs(d, dev):
@@ -235,6 +286,13 @@ def main():
         print("bench.py: the layer is measured on one GPU only (one GPU holds all experts; "
               "expert-parallel sharding is not implemented); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
+
+    if not args.no_cpu_baseline:
+        # the oracle's worker processes are forked now, before this process
+        # touches the GPU, so they hold no GPU state; they wait until the end
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        import oracle_pool
+        oracle_pool.start()
 
     cfg = CFG
     T, K, I, E, k = cfg.T, cfg.K, cfg.I, cfg.E, cfg.k
@@ -444,7 +502,11 @@ def main():
         rec["copy_calibration_bytes"] = n
         del src, dst
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(d)
+        print("bench.py: cpu baseline (the oracle on the whole layer)", file=sys.stderr, flush=True)
+        step()
+        torch.cuda.synchronize()
+        gpu_out = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        rec["cpu_baseline"] = cpu_baseline(d, gpu_out)
     print(json.dumps(rec), flush=True)
 
 

@@ -13,10 +13,10 @@ for _p in (HERE, ROOT):
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: large CPU oracle runs")
-    # the oracle's worker processes must be forked from a process that never
-    # touched the GPU: start their fork server before any test runs
+    # the oracle's worker processes must be forked from a process that has
+    # not touched the GPU: fork them before any test runs
     import oracle_pool
-    oracle_pool.start_server()
+    oracle_pool.start()
 
 
 def pytest_unconfigure(config):

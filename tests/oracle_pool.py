@@ -10,21 +10,20 @@ ascending order, one rounding to float32; the quantiser works block by
 block), so the stitched result is the bytes the oracle gives on the whole
 matrix; ``test_oracle_pool.py`` pins that on the CPU.
 
-Workers are forked from a fork server that ``start_server`` launches when
-the test session is configured, before any test touches the GPU, so no
-worker holds GPU state.  Each worker runs single-threaded BLAS (the thin
-32-wide block products run faster that way than on a shared thread pool).
+The workers are forked once, by ``start`` (called when the test session is
+configured, or at the start of the benchmark), before the process touches
+the GPU, so no worker holds GPU state; they then wait for work.  Each
+worker runs single-threaded BLAS (the thin 32-wide block products run
+faster that way than on a shared thread pool).
 """
 
 import multiprocessing as mp
 import os
-import sys
 
 import numpy as np
 
 from oracle import moe_ref, mx_ref
 
-_CTX = None
 _POOL = None
 
 
@@ -33,19 +32,12 @@ def n_workers():
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def start_server():
-    """Start the fork server now (call before the GPU is initialised)."""
-    global _CTX
-    if _CTX is not None:
-        return
-    _CTX = mp.get_context("forkserver")
-    here = os.path.dirname(os.path.abspath(__file__))
-    for p in (here, os.path.dirname(here)):
-        if p not in sys.path:
-            sys.path.insert(0, p)
-    _CTX.set_forkserver_preload(["numpy", "oracle.mx_ref", "oracle.moe_ref", "oracle_pool"])
-    from multiprocessing import forkserver
-    forkserver.ensure_running()
+def start():
+    """Fork the workers now (call before the GPU is initialised)."""
+    global _POOL
+    if _POOL is None:
+        _POOL = mp.get_context("fork").Pool(n_workers(), initializer=_init_worker)
+    return _POOL
 
 
 def _init_worker():
@@ -57,11 +49,7 @@ def _init_worker():
 
 
 def pool():
-    global _POOL
-    if _POOL is None:
-        start_server()
-        _POOL = _CTX.Pool(n_workers(), initializer=_init_worker)
-    return _POOL
+    return start()
 
 
 def shutdown():
@@ -173,3 +161,36 @@ def quantize_bf16(bits, rows=2048, fp4=False):
     for (a, b), (qq, ss) in zip(parts, pool().imap(fn, [bits[a:b] for a, b in parts])):
         q[a:b], s[a:b] = qq, ss
     return q, s
+
+
+def _w_finalize(args):
+    y_rows, w, k = args
+    n = w.shape[0]
+    return moe_ref.finalize_ref(y_rows, w, np.arange(n * k).reshape(n, k))
+
+
+def route_quant(x_bits, topk_ids, E, rows=2048):
+    """Equal to ``moe_ref.route_quant_ref``: the stable routing maps, and
+    every expanded row's MX quantisation of its token (each token quantised
+    once, by row chunks in the workers, then gathered)."""
+    ids = np.asarray(topk_ids)
+    k = ids.shape[1]
+    counts, sorted_row, eri = moe_ref.route_ref_fast(ids, E)
+    q_tok, s_tok = quantize_bf16(x_bits, rows)
+    tok = sorted_row.astype(np.int64) // k
+    return q_tok[tok], s_tok[tok], sorted_row, eri, counts
+
+
+def finalize(y_bits, topk_w, expanded_row_idx, tokens=1024):
+    """Equal to ``moe_ref.finalize_ref``: each chunk of tokens gets its own
+    k rows of y (gathered here in token order) and the oracle's finalize
+    runs on them in a worker."""
+    w = np.asarray(topk_w, np.float32)
+    T, k = w.shape
+    idx = np.asarray(expanded_row_idx).reshape(T, k)
+    parts = _chunks(T, tokens)
+    args = [(y_bits[idx[a:b].reshape(-1)], w[a:b], k) for a, b in parts]
+    out = np.empty((T, y_bits.shape[1]), np.uint16)
+    for (a, b), part in zip(parts, pool().imap(_w_finalize, args)):
+        out[a:b] = part
+    return out

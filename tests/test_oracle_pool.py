@@ -61,3 +61,17 @@ def test_pooled_quantisers_equal_the_oracle():
     q, s = oracle_pool.quantize_bf16(bits, rows=6, fp4=True)
     qr, sr = mx_ref.mxfp4_quantize_ref(mx_ref.bf16_to_f64(bits))
     assert np.array_equal(q, qr) and np.array_equal(s, sr)
+
+
+def test_pooled_routing_and_finalize_equal_the_oracle():
+    T, K, k, E = 53, 96, 3, 7
+    x = to_bf16_bits(RNG.standard_normal((T, K)).astype(np.float32))
+    ids = np.stack([RNG.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    got = oracle_pool.route_quant(x, ids, E, rows=5)
+    ref = moe_ref.route_quant_ref(x, ids, E)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g, r)
+    y = to_bf16_bits((RNG.standard_normal((T * k, K)) * np.exp2(RNG.integers(-9, 9, (T * k, 1)))).astype(np.float32))
+    w = RNG.random((T, k)).astype(np.float32)
+    eri = RNG.permutation(T * k).astype(np.int32)
+    assert np.array_equal(oracle_pool.finalize(y, w, eri, tokens=4), moe_ref.finalize_ref(y, w, eri))
