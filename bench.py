@@ -25,7 +25,8 @@ weights of w13's shape).  Last, the
 "workloads" object times the layer on all five shapes (tiny, decode, mid,
 16K prefill, wide prefill): per-step median/p10/p90, tokens/s, per-kernel
 medians and the GEMMs' TFLOP/s, plus cold-cache steps for the two small
-shapes.
+shapes, and for decode, mid and 16K prefill the same layer with tile-packed
+weights (mx_pack_weights).
 """
 
 import argparse
@@ -186,6 +187,41 @@ def _pct(v):
             "us_p90": round(float(np.percentile(v, 90)), 2)}
 
 
+def _packed_timing(x, ids, w, w13, w13s, w2, w2s, ws, out, inter, steps, stream):
+    """The same layer with tile-packed weights (mx_pack_weights, the
+    load-time cast; not timed): per-step median of moe_mxfp8_forward_packed
+    and the medians of its two GEMMs through their own entry points."""
+    w13p = mx.mx_pack_weights(w13, mx.PACK_GEMM1)
+    w2p = mx.mx_pack_weights(w2, mx.PACK_GEMM2)
+
+    def step():
+        mx.moe_mxfp8_forward_packed(x, ids, w, w13p, w13s, w2p, w2s, out=out, workspace=ws)
+
+    for _ in range(10):
+        step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    ge = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for s_ in range(steps):
+        ge[s_][0].record(stream)
+        mx.gmm_swiglu_mxquant_packed(inter["xq"], inter["xs"], w13p, w13s, inter["group_list"], 1,
+                                     out=(inter["hq"], inter["hs"]))
+        ge[s_][1].record(stream)
+        mx.gmm_mx_packed(inter["hq"], inter["hs"], w2p, w2s, inter["group_list"], 1, out=inter["y"])
+        ge[s_][2].record(stream)
+    torch.cuda.synchronize()
+    lay = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+    g = [[ge[s_][i].elapsed_time(ge[s_][i + 1]) * 1e3 for s_ in range(steps)] for i in range(2)]
+    res = _pct(lay)
+    res["kernels_us_median"] = {"gemm1_swiglu_requant": round(float(np.median(g[0])), 2),
+                                "gemm2": round(float(np.median(g[1])), 2)}
+    del w13p, w2p
+    return res
+
+
 def workload_table(dev, stream, prefill_inputs):
     """All five layer shapes on one GPU: per-step layer time (HIP events on the
     launch stream; median, p10, p90), tokens/s from the median, per-kernel
@@ -249,6 +285,8 @@ def workload_table(dev, stream, prefill_inputs):
         ent["gemm_TFLOPs"] = round(gtf, 1)
         ent["gemm_mfma_frac"] = round(gtf / MFMA_FP8_PEAK_TFLOPS, 4)
         ent["experts_hit"] = int((counts > 0).sum())
+        if name in ("decode", "mid", "prefill"):
+            ent["packed_weights"] = _packed_timing(x, ids, w, w13, w13s, w2, w2s, ws, out, inter, steps, stream)
         if small:
             flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
             cold = []
@@ -268,6 +306,101 @@ def workload_table(dev, stream, prefill_inputs):
     return table
 
 
+def profile_workload(name, warmup, steps, dev, copy_calibration):
+    """--profile-workload: only `warmup` + `steps` layer steps of one
+    workload (for counter runs under rocprofv3, one workload per process so
+    each kernel's dispatches belong to it), then optionally the 1 GiB copy
+    that calibrates FETCH_SIZE / WRITE_SIZE.  Prints one JSON line with the
+    workload's per-kernel algorithmic bytes and flops."""
+    cfg = CONFIGS[name]
+    T, K, I, E, k = cfg.T, cfg.K, cfg.I, cfg.E, cfg.k
+    x, ids, w, w13, w13s, w2, w2s = _dev_inputs(make_inputs(cfg), dev)
+    ws = mx.forward_workspace(T, K, I, E, k, dev)
+    out = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+    for _ in range(warmup + steps):
+        mx.moe_mxfp8_forward(x, ids, w, w13, w13s, w2, w2s, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    counts = mx.forward_intermediates(ws, T, K, I, E, k)["group_list"].cpu().numpy()
+    if copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    print(json.dumps({"profile_workload": name, "T": T, "K": K, "I": I, "E": E, "top_k": k, "forward_steps":
+                      warmup + steps, "experts_hit": int((counts > 0).sum()),
+                      "algorithmic": algorithmic(cfg, counts)}), flush=True)
+
+
+# rocprofv3 kernel names of the layer's kernels -> the step they implement
+_STEP_OF = {"route_hist": "route_quant", "route_scan": "route_quant", "route_scatter_quant": "route_quant",
+            "gmm_kernel<true, false, 4, 256>": "gemm1_swiglu_requant",
+            "gmm_kernel<true, false, 1, 256>": "gemm1_swiglu_requant",
+            "gmm_kernel<true, false, 1, 128>": "gemm1_swiglu_requant",
+            "gmm_kernel<false, false, 4, 256>": "gemm2", "gmm_kernel<false, false, 1, 256>": "gemm2",
+            "gmm_kernel<false, false, 1, 128>": "gemm2",
+            "finalize_kernel<true>": "finalize", "finalize_kernel<false>": "finalize"}
+
+
+def counter_summary(name, fetch_dir, write_dir, sq_dir, tcc_dir):
+    """--counter-summary: markdown tables from four rocprofv3 --pmc runs of
+    `--profile-workload name --copy-calibration` (FETCH_SIZE; WRITE_SIZE;
+    SQ and GRBM counters; TCC hit/miss), per kernel: HBM bytes per dispatch
+    calibrated on the 1 GiB copies, against the kernel's algorithmic bytes;
+    shader clock; MFMA busy; LDS bank conflicts; L2 hit rate."""
+    import csv
+    import glob
+    import re
+
+    def load(d):
+        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        disp = {}
+        for r in csv.DictReader(open(path)):
+            n = re.sub(r"\(.*$", "", r["Kernel_Name"].replace("void ", "").replace(
+                "mxmoe::(anonymous namespace)::", ""))
+            e = disp.setdefault(r["Dispatch_Id"], {"name": n, "dur_us": (int(r["End_Timestamp"]) -
+                                                                          int(r["Start_Timestamp"])) / 1e3})
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        per = {}
+        for e in disp.values():
+            per.setdefault(e["name"], []).append(e)
+        return per
+
+    cfg = CONFIGS[name]
+    d = make_inputs(cfg, weights=False)
+    counts = np.bincount(d["topk_ids"].reshape(-1), minlength=cfg.E)
+    alg = algorithmic(cfg, counts)
+    fe, wr, sq, tc = load(fetch_dir), load(write_dir), load(sq_dir), load(tcc_dir)
+    cf = [e["FETCH_SIZE"] for e in fe.get("__amd_rocclr_copyBuffer", []) if e["FETCH_SIZE"] > 1e5]
+    cw = [e["WRITE_SIZE"] for e in wr.get("__amd_rocclr_copyBuffer", []) if e["WRITE_SIZE"] > 1e5]
+    ff, fw = 1048576 / np.mean(cf), 1048576 / np.mean(cw)
+    lines = [f"Calibration: {len(cf)} copies of 1 GiB; FETCH_SIZE reads {np.mean(cf):.0f} KiB and WRITE_SIZE "
+             f"{np.mean(cw):.0f} KiB per copy, so bytes = FETCH_SIZE x 1024 x {ff:.4f} and WRITE_SIZE x 1024 x "
+             f"{fw:.4f}.", "",
+             "| kernel | step | dispatches | avg µs | read MB | written MB | total MB | algorithmic MB (step) | "
+             "ratio | clock GHz | MFMA busy | LDS bank conflict | L2 hit rate |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in fe:
+        if k.startswith("__amd") or k not in _STEP_OF:
+            continue
+        st = _STEP_OF[k]
+        rd = np.mean([e["FETCH_SIZE"] for e in fe[k]]) * 1024 * ff / 1e6
+        wt = np.mean([e["WRITE_SIZE"] for e in wr[k]]) * 1024 * fw / 1e6
+        S = sq[k]
+        dur = np.mean([e["dur_us"] for e in S])
+        gui = np.mean([e["GRBM_GUI_ACTIVE"] for e in S])
+        clk = gui / 8 / (dur * 1e3)
+        mf = np.mean([e["SQ_VALU_MFMA_BUSY_CYCLES"] for e in S]) / (1024 * gui / 8)
+        lds = sum(e["SQ_LDS_BANK_CONFLICT"] for e in S) / max(1.0, sum(e["SQ_LDS_IDX_ACTIVE"] for e in S))
+        hit = sum(e["TCC_HIT_sum"] for e in tc[k])
+        miss = sum(e["TCC_MISS_sum"] for e in tc[k])
+        a = alg[st]["bytes"] / 1e6
+        ratio = f"{(rd + wt) / a:.2f}" if k not in ("route_hist", "route_scan") else ""
+        lines.append(f"| {k} | {st} | {len(fe[k])} | {dur:.1f} | {rd:.1f} | {wt:.1f} | {rd + wt:.1f} | {a:.1f} | "
+                     f"{ratio} | {clk:.2f} | {mf:.3f} | {lds:.3f} | {hit / max(1.0, hit + miss):.3f} |")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,12 +414,24 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with a 1 GiB device-to-device copy, the known-size kernel that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE hardware counters")
+    ap.add_argument("--profile-workload", choices=list(CONFIGS),
+                    help="only run this workload's layer (--warmup + --steps steps), for counter runs")
+    ap.add_argument("--counter-summary", nargs=5, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "SQ_DIR", "TCC_DIR"),
+                    help="print counter tables from four rocprofv3 --pmc runs of --profile-workload (no GPU)")
     args = ap.parse_args()
+    if args.counter_summary:
+        counter_summary(*args.counter_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: the layer is measured on one GPU only (one GPU holds all experts; "
               "expert-parallel sharding is not implemented); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.profile_workload:
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        profile_workload(args.profile_workload, args.warmup, args.steps, dev, args.copy_calibration)
+        return
     if not args.no_cpu_baseline:
         # the oracle's worker processes are forked now, before this process
         # touches the GPU, so they hold no GPU state; they wait until the end

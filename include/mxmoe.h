@@ -17,6 +17,10 @@
  *   moe_router          top-k softmax router over a bf16 gate (upstream of
  *                       the layer: produces the ids and weights it takes)
  *   mx_linear           dense MXFP8 linear layer (activation quant + MX GEMM)
+ *   mx_pack_weights, gmm_swiglu_mxquant_packed, gmm_mx_packed,
+ *   moe_mxfp8_forward_packed
+ *                       load-time weight cast into the GEMMs' tile layout,
+ *                       and the GEMMs and the layer reading it
  *   mx_quantize_fp4     MXFP4 (e2m1) quantiser for the W4A8 path's weights
  *   gmm_swiglu_mxquant_w4a8, gmm_mx_w4a8, moe_w4a8_forward
  *                       the GEMMs and the layer with MXFP4 expert weights
@@ -207,6 +211,43 @@ int gmm_mx(const void* a_u8, const void* a_s, const void* w_u8, const void* w_s,
            void* y_bf16, void* stream);
 
 /*
+ * Tile-packed expert weights: the weights' load-time cast into the layout
+ * the GEMMs' LDS ring holds, the counterpart of the pages' cast of expert
+ * weights into the matrix unit's tiled format once at load ("PR #30768
+ * report", review highlights: the NZ format; PR 32266, the commit casting
+ * weights to NZ).  mx_pack_weights rewrites e4m3 weights w [E, N, Kd] into
+ * out (same size, E*N*Kd bytes, must not overlap w): for expert e, n-tile
+ * nt = 0 .. N/256 - 1 and k stage ks = 0 .. Kd/128 - 1, the 32 KB block at
+ * byte ((e*(N/256) + nt)*(Kd/128) + ks)*32768 holds 256 rows of 128 bytes,
+ * 16-byte chunk c of block row r at chunk position c ^ ((r/2) % 8).  Block
+ * row r is weight row 256*nt + r for kind 0 (GEMM2 weights w2 [E, K, I]);
+ * for kind 1 (GEMM1 weights w13 [E, 2I, K], I = N/2) block rows
+ * [128h, 128h+64) are gate rows 128*nt + 64h + (0..63) and block rows
+ * [128h+64, 128h+128) up rows I + 128*nt + 64h + (0..63), h = 0, 1.
+ * Scales are not packed: the *_packed calls take them in the usual
+ * [E, N, Kd/64, 2] layout.  Needs N % 256 == 0, Kd % 128 == 0, E <= 1024.
+ *
+ * gmm_swiglu_mxquant_packed, gmm_mx_packed and moe_mxfp8_forward_packed
+ * are gmm_swiglu_mxquant, gmm_mx and moe_mxfp8_forward with w13 packed as
+ * kind 1 and w2 (w) packed as kind 0; arguments, results and limits are
+ * otherwise the same (the results are identical byte for byte).
+ */
+int mx_pack_weights(const void* w_u8, int64_t E, int64_t N, int64_t Kd, int kind,
+                    void* out_u8, void* stream);
+
+int gmm_swiglu_mxquant_packed(const void* a_u8, const void* a_s,
+                              const void* w13_packed, const void* w13_s,
+                              const int64_t* group_list, int group_list_type,
+                              int64_t M, int64_t K, int64_t I, int64_t E,
+                              void* hq_u8, void* hs_u8, float* h_f32_debug,
+                              void* stream);
+
+int gmm_mx_packed(const void* a_u8, const void* a_s, const void* w_packed,
+                  const void* w_s, const int64_t* group_list, int group_list_type,
+                  int64_t M, int64_t N, int64_t Kd, int64_t E, void* y_bf16,
+                  void* stream);
+
+/*
  * Finalize: weighted un-permute and sum (PR 32266, fused-experts commit:
  * the chain ends with finalize routing).
  *   out[t, :] = bf16_rne( sum_{j=0}^{k-1} w[t, j] * y[expanded_row_idx[t*k+j], :] )
@@ -254,6 +295,14 @@ int moe_mxfp8_forward(const void* x_bf16, const int32_t* topk_ids,
                       int64_t T, int64_t K, int64_t I, int64_t E, int64_t k,
                       void* out_bf16, void* workspace, size_t ws_bytes,
                       void* stream);
+
+/* moe_mxfp8_forward with tile-packed weights (see mx_pack_weights). */
+int moe_mxfp8_forward_packed(const void* x_bf16, const int32_t* topk_ids,
+                             const float* topk_w, const void* w13_packed,
+                             const void* w13_s, const void* w2_packed,
+                             const void* w2_s, int64_t T, int64_t K, int64_t I,
+                             int64_t E, int64_t k, void* out_bf16, void* workspace,
+                             size_t ws_bytes, void* stream);
 
 /*
  * The whole layer with MXFP4 expert weights (the W4A8 path): as

@@ -23,7 +23,8 @@ __all__ = [
     "MxError", "lib_path", "load", "mx_quantize", "moe_route_quant", "gmm_swiglu_mxquant",
     "gmm_mx", "moe_finalize", "moe_mxfp8_forward", "forward_workspace", "forward_intermediates",
     "route_workspace_size", "forward_workspace_size", "last_error", "moe_router", "mx_linear",
-    "linear_workspace_size", "mx_quantize_fp4", "moe_route_quant_noalloc", "gmm_mx_w4a8", "gmm_swiglu_mxquant_w4a8", "moe_w4a8_forward",
+    "linear_workspace_size", "mx_quantize_fp4", "moe_route_quant_noalloc", "mx_pack_weights",
+    "gmm_swiglu_mxquant_packed", "gmm_mx_packed", "moe_mxfp8_forward_packed", "gmm_mx_w4a8", "gmm_swiglu_mxquant_w4a8", "moe_w4a8_forward",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +73,10 @@ def load():
         "moe_router": (I32, [P, P, P, I64, I64, I64, I64, I32, P, P, P]),
         "mx_linear_workspace_size": (SZ, [I64, I64]),
         "mx_linear": (I32, [P, P, P, I64, I64, I64, P, P, SZ, P]),
+        "mx_pack_weights": (I32, [P, I64, I64, I64, I32, P, P]),
+        "gmm_swiglu_mxquant_packed": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P, P, P]),
+        "gmm_mx_packed": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]),
+        "moe_mxfp8_forward_packed": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
         "mx_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -263,7 +268,7 @@ def moe_route_quant_noalloc(x, topk_ids, E, out=None, stream=None):
 
 @_stream_scoped
 def gmm_swiglu_mxquant(a, a_s, w13, w13_s, group_list, group_list_type=GROUP_COUNT, out=None,
-                       h_debug=False, stream=None, _w4=False):
+                       h_debug=False, stream=None, _w4=False, _packed=False):
     """GEMM1 + SwiGLU + MX requant.  Returns (hq, hs) or (hq, hs, h) with h_debug."""
     _need(a, torch.uint8, "a", 2); _need(w13, torch.uint8, "w13", 3)
     M, K = a.shape
@@ -286,15 +291,16 @@ def gmm_swiglu_mxquant(a, a_s, w13, w13_s, group_list, group_list_type=GROUP_COU
     _need_shape(hs, (M, _pairs(I), 2), "hs", torch.uint8, dev)
     h = torch.empty((M, I), dtype=torch.float32, device=dev) if h_debug else None
     _need_gpu(a, "a")
-    fn = load().gmm_swiglu_mxquant_w4a8 if _w4 else load().gmm_swiglu_mxquant
-    rc = fn(_ptr(a), _ptr(a_s), _ptr(w13), _ptr(w13_s), _ptr(group_list), group_list_type, M, K, I, E, _ptr(hq),
-            _ptr(hs), _ptr(h), _stream(stream))
-    _check(rc, "gmm_swiglu_mxquant_w4a8" if _w4 else "gmm_swiglu_mxquant")
+    name = "gmm_swiglu_mxquant_w4a8" if _w4 else "gmm_swiglu_mxquant_packed" if _packed else "gmm_swiglu_mxquant"
+    rc = getattr(load(), name)(_ptr(a), _ptr(a_s), _ptr(w13), _ptr(w13_s), _ptr(group_list), group_list_type, M, K,
+                               I, E, _ptr(hq), _ptr(hs), _ptr(h), _stream(stream))
+    _check(rc, name)
     return (hq, hs, h) if h_debug else (hq, hs)
 
 
 @_stream_scoped
-def gmm_mx(a, a_s, w, w_s, group_list, group_list_type=GROUP_COUNT, out=None, stream=None, _w4=False):
+def gmm_mx(a, a_s, w, w_s, group_list, group_list_type=GROUP_COUNT, out=None, stream=None, _w4=False,
+           _packed=False):
     """Grouped MX GEMM, bf16 output [M, N]."""
     _need(a, torch.uint8, "a", 2); _need(w, torch.uint8, "w", 3)
     M, Kd = a.shape
@@ -312,10 +318,10 @@ def gmm_mx(a, a_s, w, w_s, group_list, group_list_type=GROUP_COUNT, out=None, st
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _need_shape(out, (M, N), "out", torch.bfloat16, dev)
     _need_gpu(a, "a")
-    fn = load().gmm_mx_w4a8 if _w4 else load().gmm_mx
-    rc = fn(_ptr(a), _ptr(a_s), _ptr(w), _ptr(w_s), _ptr(group_list), group_list_type, M, N, Kd, E, _ptr(out),
-            _stream(stream))
-    _check(rc, "gmm_mx_w4a8" if _w4 else "gmm_mx")
+    name = "gmm_mx_w4a8" if _w4 else "gmm_mx_packed" if _packed else "gmm_mx"
+    rc = getattr(load(), name)(_ptr(a), _ptr(a_s), _ptr(w), _ptr(w_s), _ptr(group_list), group_list_type, M, N, Kd,
+                               E, _ptr(out), _stream(stream))
+    _check(rc, name)
     return out
 
 
@@ -352,7 +358,7 @@ def forward_workspace(T, K, I, E, k, device="cuda"):
 
 @_stream_scoped
 def moe_mxfp8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, workspace=None, stream=None,
-                      _w4=False):
+                      _w4=False, _packed=False):
     """The whole layer.  x [T,K] bf16, topk_ids [T,k] i32, topk_w [T,k] f32,
     w13 [E,2I,K] u8 + w13_s [E,2I,K/64,2], w2 [E,K,I] u8 + w2_s [E,K,I/64,2].
     Returns out [T,K] bf16."""
@@ -381,10 +387,10 @@ def moe_mxfp8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, works
         workspace = forward_workspace(T, K, I, E, k, dev)
     _need_workspace(workspace, need, dev)
     _need_gpu(x, "x")
-    fn = load().moe_w4a8_forward if _w4 else load().moe_mxfp8_forward
-    rc = fn(_ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w13), _ptr(w13_s), _ptr(w2), _ptr(w2_s), T, K, I, E, k,
-            _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
-    _check(rc, "moe_w4a8_forward" if _w4 else "moe_mxfp8_forward")
+    name = "moe_w4a8_forward" if _w4 else "moe_mxfp8_forward_packed" if _packed else "moe_mxfp8_forward"
+    rc = getattr(load(), name)(_ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w13), _ptr(w13_s), _ptr(w2), _ptr(w2_s),
+                               T, K, I, E, k, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, name)
     return out
 
 
@@ -510,3 +516,43 @@ def gmm_mx_w4a8(a, a_s, w, w_s, group_list, group_list_type=GROUP_COUNT, out=Non
 def moe_w4a8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, workspace=None, stream=None):
     """The layer with MXFP4 expert weights: w13 [E,2I,K/2], w2 [E,K,I/2] packed e2m1."""
     return moe_mxfp8_forward(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out, workspace, stream, _w4=True)
+
+
+PACK_GEMM2 = 0   # mx_pack_weights kind: plain weight rows (w2, the dense linear)
+PACK_GEMM1 = 1   # mx_pack_weights kind: w13, gate rows then up rows
+
+
+@_stream_scoped
+def mx_pack_weights(w, kind, out=None, stream=None):
+    """e4m3 expert weights w [E, N, Kd] uint8 -> the tile-packed layout the
+    *_packed GEMMs read (same shape and size; see include/mxmoe.h).
+    kind: PACK_GEMM1 for w13 [E, 2I, K], PACK_GEMM2 for w2 [E, K, I]."""
+    _need(w, torch.uint8, "w", 3)
+    E, N, Kd = w.shape
+    if out is None:
+        out = torch.empty_like(w)
+    _need_shape(w, (E, N, Kd), "w", torch.uint8, w.device)
+    _need_shape(out, (E, N, Kd), "out", torch.uint8, w.device)
+    _need_gpu(w, "w")
+    rc = load().mx_pack_weights(_ptr(w), E, N, Kd, int(kind), _ptr(out), _stream(stream))
+    _check(rc, "mx_pack_weights")
+    return out
+
+
+def gmm_swiglu_mxquant_packed(a, a_s, w13_packed, w13_s, group_list, group_list_type=GROUP_COUNT, out=None,
+                              h_debug=False, stream=None):
+    """gmm_swiglu_mxquant with w13 tile-packed (mx_pack_weights, PACK_GEMM1)."""
+    return gmm_swiglu_mxquant(a, a_s, w13_packed, w13_s, group_list, group_list_type, out, h_debug, stream,
+                              _packed=True)
+
+
+def gmm_mx_packed(a, a_s, w_packed, w_s, group_list, group_list_type=GROUP_COUNT, out=None, stream=None):
+    """gmm_mx with w tile-packed (mx_pack_weights, PACK_GEMM2)."""
+    return gmm_mx(a, a_s, w_packed, w_s, group_list, group_list_type, out, stream, _packed=True)
+
+
+def moe_mxfp8_forward_packed(x, topk_ids, topk_w, w13_packed, w13_s, w2_packed, w2_s, out=None, workspace=None,
+                             stream=None):
+    """moe_mxfp8_forward with w13 and w2 tile-packed by mx_pack_weights."""
+    return moe_mxfp8_forward(x, topk_ids, topk_w, w13_packed, w13_s, w2_packed, w2_s, out, workspace, stream,
+                             _packed=True)

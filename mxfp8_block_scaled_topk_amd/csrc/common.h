@@ -27,6 +27,11 @@ int num_cus();
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Expert-weight formats of the grouped GEMMs: e4m3 rows [E, N, Kd]; MXFP4
+// (packed e2m1) rows [E, N, Kd/2]; e4m3 in the tile-packed layout that
+// mx_pack_weights writes.
+constexpr int kWfE4m3 = 0, kWfE2m1 = 1, kWfPacked = 2;
+
 // Largest value any size argument may take (MX_ERR_UNSUPPORTED above it).
 // With every dimension at most 2^31 - 1, the host's products of two sizes
 // stay far inside int64_t, so no size arithmetic can overflow.

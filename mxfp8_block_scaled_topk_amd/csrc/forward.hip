@@ -17,10 +17,10 @@ int launch_route_quant(const uint16_t* x, const int32_t* ids, int64_t T, int64_t
 int check_gmm_common(const char* name, int gl_type, int64_t M, int64_t Kd, int64_t E);
 int launch_gmm_swiglu(const uint8_t* a, const uint8_t* as, const uint8_t* w13, const uint8_t* w13s,
                       const int64_t* gl, int gl_type, int64_t M, int64_t K, int64_t I, int64_t E, uint8_t* hq,
-                      uint8_t* hs, float* hdbg, hipStream_t stream, bool w4);
+                      uint8_t* hs, float* hdbg, hipStream_t stream, int wf);
 int launch_gmm_mx(const uint8_t* a, const uint8_t* as, const uint8_t* w, const uint8_t* ws, const int64_t* gl,
                   int gl_type, int64_t M, int64_t N, int64_t Kd, int64_t E, uint16_t* y, hipStream_t stream,
-                  bool w4);
+                  int wf);
 int launch_finalize(const uint16_t* y, const float* w, const int32_t* eri, int64_t T, int64_t K, int64_t k,
                     int64_t M, uint16_t* out, hipStream_t stream);
 
@@ -88,9 +88,10 @@ extern "C" int moe_mxfp8_forward_workspace_layout(int64_t T, int64_t K, int64_t 
 
 namespace {
 
-// The layer on one stream; w4: the expert weights are MXFP4 (packed e2m1,
-// the W4A8 path), the activations are MXFP8 either way.
-int forward(const char* name, bool w4, const void* x_bf16, const int32_t* topk_ids, const float* topk_w,
+// The layer on one stream; wf: the expert weights' format (e4m3 rows, MXFP4
+// packed e2m1 for the W4A8 path, or e4m3 tile-packed by mx_pack_weights);
+// the activations are MXFP8 either way.
+int forward(const char* name, int wf, const void* x_bf16, const int32_t* topk_ids, const float* topk_w,
             const void* w13_u8, const void* w13_s, const void* w2_u8, const void* w2_s, int64_t T, int64_t K,
             int64_t I, int64_t E, int64_t k, void* out_bf16, void* workspace, size_t ws_bytes, void* stream) {
   using namespace mxmoe;
@@ -125,10 +126,10 @@ int forward(const char* name, bool w4, const void* x_bf16, const int32_t* topk_i
                           rws, s);
   if (rc) return rc;
   rc = launch_gmm_swiglu(xq, xs, static_cast<const uint8_t*>(w13_u8), static_cast<const uint8_t*>(w13_s), gl, 1, M,
-                         K, I, E, hq, hs, nullptr, s, w4);
+                         K, I, E, hq, hs, nullptr, s, wf);
   if (rc) return rc;
   rc = launch_gmm_mx(hq, hs, static_cast<const uint8_t*>(w2_u8), static_cast<const uint8_t*>(w2_s), gl, 1, M, K, I,
-                     E, y, s, w4);
+                     E, y, s, wf);
   if (rc) return rc;
   return launch_finalize(y, topk_w, eri, T, K, k, M, static_cast<uint16_t*>(out_bf16), s);
 }
@@ -139,7 +140,7 @@ extern "C" int moe_mxfp8_forward(const void* x_bf16, const int32_t* topk_ids, co
                                  const void* w13_u8, const void* w13_s, const void* w2_u8, const void* w2_s,
                                  int64_t T, int64_t K, int64_t I, int64_t E, int64_t k, void* out_bf16,
                                  void* workspace, size_t ws_bytes, void* stream) {
-  return forward("moe_mxfp8_forward", false, x_bf16, topk_ids, topk_w, w13_u8, w13_s, w2_u8, w2_s, T, K, I, E, k,
+  return forward("moe_mxfp8_forward", mxmoe::kWfE4m3, x_bf16, topk_ids, topk_w, w13_u8, w13_s, w2_u8, w2_s, T, K, I, E, k,
                  out_bf16, workspace, ws_bytes, stream);
 }
 
@@ -147,6 +148,14 @@ extern "C" int moe_w4a8_forward(const void* x_bf16, const int32_t* topk_ids, con
                                 const void* w13_u8, const void* w13_s, const void* w2_u8, const void* w2_s,
                                 int64_t T, int64_t K, int64_t I, int64_t E, int64_t k, void* out_bf16,
                                 void* workspace, size_t ws_bytes, void* stream) {
-  return forward("moe_w4a8_forward", true, x_bf16, topk_ids, topk_w, w13_u8, w13_s, w2_u8, w2_s, T, K, I, E, k,
+  return forward("moe_w4a8_forward", mxmoe::kWfE2m1, x_bf16, topk_ids, topk_w, w13_u8, w13_s, w2_u8, w2_s, T, K, I, E, k,
                  out_bf16, workspace, ws_bytes, stream);
+}
+
+extern "C" int moe_mxfp8_forward_packed(const void* x_bf16, const int32_t* topk_ids, const float* topk_w,
+                                        const void* w13_packed, const void* w13_s, const void* w2_packed,
+                                        const void* w2_s, int64_t T, int64_t K, int64_t I, int64_t E, int64_t k,
+                                        void* out_bf16, void* workspace, size_t ws_bytes, void* stream) {
+  return forward("moe_mxfp8_forward_packed", mxmoe::kWfPacked, x_bf16, topk_ids, topk_w, w13_packed, w13_s,
+                 w2_packed, w2_s, T, K, I, E, k, out_bf16, workspace, ws_bytes, stream);
 }

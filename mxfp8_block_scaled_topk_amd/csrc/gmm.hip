@@ -203,8 +203,13 @@ struct TileInfo {
 // Physical 16-byte chunk of logical chunk c in tile row r (128-byte rows).
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// kW4: the weights are MXFP4 (packed e2m1, Kd/2 bytes per row, the W4A8
-// path); the token operand stays MXFP8.
+// kWF: the weights' format and layout.  kWfE4m3: e4m3 rows [E, Nw, Kd].
+// kWfE2m1: MXFP4 (packed e2m1, Kd/2 bytes per row, the W4A8 path); the
+// token operand stays MXFP8.  kWfPacked: e4m3 in the tile-packed layout of
+// mx_pack_weights -- for every (expert, n-tile, k stage) the 256 x 128
+// bytes a workgroup's ring slot receives, stored contiguously in the slot's
+// own row order with each row's 16-byte chunks already swizzled, so a
+// stage's weight DMA reads one contiguous 32 KB block.
 // kG: k stages per scale load.  kG = 1: every stage's DMA brings the 4 scale
 // bytes per row of that stage (a 64-lane dword load touches 32 lines for
 // 256 bytes).  kG = 4 (k stages a multiple of 4, scale rows 16-byte
@@ -216,8 +221,10 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 // rather than MFMA-bound): each wave holds one 32-token fragment, a slot is
 // 49.5 KB, and three slots give the DMA two stages of lead; per-stage scale
 // loads only (the scale ring would not fit) and at least 3 k stages.
-template <bool kSwiglu, bool kW4, int kG, int kBM>
+template <bool kSwiglu, int kWF, int kG, int kBM>
 __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
+  constexpr bool kW4 = kWF == kWfE2m1;
+  constexpr bool kPk = kWF == kWfPacked;
   static_assert(kG == 1 || kG == 4, "scale groups of 1 or 4 stages");
   static_assert(kBM == 256 || (kBM == 128 && kG == 1), "128-row tiles use per-stage scale loads");
   constexpr int kSl = kBM == 256 ? 2 : 3;   // LDS ring slots
@@ -373,7 +380,10 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       sbase = (int64_t)ti.nt * BN + 64 * (wave & 3);
     }
     const int64_t wr = (int64_t)ti.e * p.Nw;
-    s.wrow = uniptr(p.w + (wr + wbase) * (kW4 ? Kd / 2 : Kd));
+    if constexpr (kPk)   // the tile's first 32 KB stage block
+      s.wrow = uniptr(p.w + ((int64_t)ti.e * n_tiles + ti.nt) * (int64_t)nk * (BN * SK));
+    else
+      s.wrow = uniptr(p.w + (wr + wbase) * (kW4 ? Kd / 2 : Kd));
     s.arow = uniptr(p.a + ti.m0 * Kd);
     s.srowp = wave < 4 ? uniptr(p.ws + (wr + sbase) * srow) : uniptr(p.as + ti.m0 * srow);
     s.last = uni((int)std::min<int64_t>(p.M - 1 - ti.m0, kBM - 1));
@@ -455,6 +465,10 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       if constexpr (kW4) {
         dma16(lane_off_a4 + (uint32_t)(8 * i * Kd) + (uint32_t)(kr * (SK / 2)), src.wrow,
               base + (uint32_t)offsetof(Stage, a) + (uint32_t)((32 * wave + 16 * i) * (SK / 2)));
+      } else if constexpr (kPk) {
+        // 1 KB contiguous: slot rows 32 wave + 8 i .. + 8, chunks as stored
+        dma16((uint32_t)(kr * (BN * SK)) + (uint32_t)((32 * wave + 8 * i) * SK) + (uint32_t)(lane * 16), src.wrow,
+              base + (uint32_t)offsetof(Stage, a) + (uint32_t)((32 * wave + 8 * i) * SK));
       } else {
         dma16(((i & 1) ? lane_off_odd : lane_off_even) + (uint32_t)(8 * i * Kd) + ko, src.wrow,
               base + (uint32_t)offsetof(Stage, a) + (uint32_t)((32 * wave + 8 * i) * SK));
@@ -834,7 +848,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
 // top-8 of 128) the 128-row tiles were 2 % slower.
 constexpr int64_t kSmallRowsPerExpert = 64;
 
-template <bool kSwiglu, bool kW4>
+template <bool kSwiglu, int kWF>
 int launch(const GmmParams& p, hipStream_t stream, const char* name) {
   if (p.M == 0) return MX_OK;
   const bool small = p.Kd / BK >= 3 && p.gl_type != kGlSingle && p.M <= kSmallRowsPerExpert * p.E;
@@ -845,7 +859,7 @@ int launch(const GmmParams& p, hipStream_t stream, const char* name) {
   if (grid < 8) grid = 8;
   if (grid > (upper + 7) / 8 * 8) grid = (upper + 7) / 8 * 8;
   if (small) {
-    gmm_kernel<kSwiglu, kW4, 1, 128><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    gmm_kernel<kSwiglu, kWF, 1, 128><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
     return check_launch(name);
   }
   // scale groups of 4 stages when the k stages divide into them and both
@@ -853,9 +867,9 @@ int launch(const GmmParams& p, hipStream_t stream, const char* name) {
   const bool groups = (p.Kd / BK) % 4 == 0 && reinterpret_cast<uintptr_t>(p.as) % 16 == 0 &&
                       reinterpret_cast<uintptr_t>(p.ws) % 16 == 0;
   if (groups)
-    gmm_kernel<kSwiglu, kW4, 4, 256><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    gmm_kernel<kSwiglu, kWF, 4, 256><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
   else
-    gmm_kernel<kSwiglu, kW4, 1, 256><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    gmm_kernel<kSwiglu, kWF, 1, 256><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
   return check_launch(name);
 }
 
@@ -880,22 +894,25 @@ int check_gmm_common(const char* name, int gl_type, int64_t M, int64_t Kd, int64
 
 int launch_gmm_mx(const uint8_t* a, const uint8_t* as, const uint8_t* w, const uint8_t* ws,
                   const int64_t* gl, int gl_type, int64_t M, int64_t N, int64_t Kd, int64_t E, uint16_t* y,
-                  hipStream_t stream, bool w4) {
+                  hipStream_t stream, int wf) {
   GmmParams p{};
   p.a = a; p.as = as; p.w = w; p.ws = ws; p.group_list = gl; p.gl_type = gl_type;
   p.E = (int)E; p.M = M; p.Kd = Kd; p.Nw = N; p.n_tiles = (int)(N / BN); p.y = y;
-  return w4 ? launch<false, true>(p, stream, "gmm_mx_w4a8") : launch<false, false>(p, stream, "gmm_mx");
+  if (wf == kWfE2m1) return launch<false, kWfE2m1>(p, stream, "gmm_mx_w4a8");
+  if (wf == kWfPacked) return launch<false, kWfPacked>(p, stream, "gmm_mx_packed");
+  return launch<false, kWfE4m3>(p, stream, "gmm_mx");
 }
 
 int launch_gmm_swiglu(const uint8_t* a, const uint8_t* as, const uint8_t* w13, const uint8_t* w13s,
                       const int64_t* gl, int gl_type, int64_t M, int64_t K, int64_t I, int64_t E, uint8_t* hq,
-                      uint8_t* hs, float* hdbg, hipStream_t stream, bool w4) {
+                      uint8_t* hs, float* hdbg, hipStream_t stream, int wf) {
   GmmParams p{};
   p.a = a; p.as = as; p.w = w13; p.ws = w13s; p.group_list = gl; p.gl_type = gl_type;
   p.E = (int)E; p.M = M; p.Kd = K; p.Nw = 2 * I; p.n_tiles = (int)(I / (BN / 2)); p.I = I;
   p.hq = hq; p.hs = hs; p.hdbg = hdbg;
-  return w4 ? launch<true, true>(p, stream, "gmm_swiglu_mxquant_w4a8")
-            : launch<true, false>(p, stream, "gmm_swiglu_mxquant");
+  if (wf == kWfE2m1) return launch<true, kWfE2m1>(p, stream, "gmm_swiglu_mxquant_w4a8");
+  if (wf == kWfPacked) return launch<true, kWfPacked>(p, stream, "gmm_swiglu_mxquant_packed");
+  return launch<true, kWfE4m3>(p, stream, "gmm_swiglu_mxquant");
 }
 
 }  // namespace mxmoe
@@ -903,7 +920,7 @@ int launch_gmm_swiglu(const uint8_t* a, const uint8_t* as, const uint8_t* w13, c
 namespace {
 
 // Host checks shared by the e4m3 and e2m1 (W4A8) entry points of GEMM2.
-int gmm_mx_entry(const char* name, bool w4, const void* a_u8, const void* a_s, const void* w_u8, const void* w_s,
+int gmm_mx_entry(const char* name, int wf, const void* a_u8, const void* a_s, const void* w_u8, const void* w_s,
                  const int64_t* group_list, int group_list_type, int64_t M, int64_t N, int64_t Kd, int64_t E,
                  void* y_bf16, void* stream) {
   using namespace mxmoe;
@@ -920,11 +937,11 @@ int gmm_mx_entry(const char* name, bool w4, const void* a_u8, const void* a_s, c
     return fail(MX_ERR_UNSUPPORTED, "%s: misaligned pointer", name);
   return launch_gmm_mx(static_cast<const uint8_t*>(a_u8), static_cast<const uint8_t*>(a_s),
                        static_cast<const uint8_t*>(w_u8), static_cast<const uint8_t*>(w_s), group_list,
-                       group_list_type, M, N, Kd, E, static_cast<uint16_t*>(y_bf16), as_stream(stream), w4);
+                       group_list_type, M, N, Kd, E, static_cast<uint16_t*>(y_bf16), as_stream(stream), wf);
 }
 
 // Host checks shared by the e4m3 and e2m1 (W4A8) entry points of GEMM1.
-int gmm_swiglu_entry(const char* name, bool w4, const void* a_u8, const void* a_s, const void* w13_u8,
+int gmm_swiglu_entry(const char* name, int wf, const void* a_u8, const void* a_s, const void* w13_u8,
                      const void* w13_s, const int64_t* group_list, int group_list_type, int64_t M, int64_t K,
                      int64_t I, int64_t E, void* hq_u8, void* hs_u8, float* h_f32_debug, void* stream) {
   using namespace mxmoe;
@@ -944,7 +961,7 @@ int gmm_swiglu_entry(const char* name, bool w4, const void* a_u8, const void* a_
   return launch_gmm_swiglu(static_cast<const uint8_t*>(a_u8), static_cast<const uint8_t*>(a_s),
                            static_cast<const uint8_t*>(w13_u8), static_cast<const uint8_t*>(w13_s), group_list,
                            group_list_type, M, K, I, E, static_cast<uint8_t*>(hq_u8),
-                           static_cast<uint8_t*>(hs_u8), h_f32_debug, as_stream(stream), w4);
+                           static_cast<uint8_t*>(hs_u8), h_f32_debug, as_stream(stream), wf);
 }
 
 }  // namespace
@@ -952,14 +969,14 @@ int gmm_swiglu_entry(const char* name, bool w4, const void* a_u8, const void* a_
 extern "C" int gmm_mx(const void* a_u8, const void* a_s, const void* w_u8, const void* w_s,
                       const int64_t* group_list, int group_list_type, int64_t M, int64_t N, int64_t Kd,
                       int64_t E, void* y_bf16, void* stream) {
-  return gmm_mx_entry("gmm_mx", false, a_u8, a_s, w_u8, w_s, group_list, group_list_type, M, N, Kd, E, y_bf16,
+  return gmm_mx_entry("gmm_mx", mxmoe::kWfE4m3, a_u8, a_s, w_u8, w_s, group_list, group_list_type, M, N, Kd, E, y_bf16,
                       stream);
 }
 
 extern "C" int gmm_mx_w4a8(const void* a_u8, const void* a_s, const void* w_u8, const void* w_s,
                            const int64_t* group_list, int group_list_type, int64_t M, int64_t N, int64_t Kd,
                            int64_t E, void* y_bf16, void* stream) {
-  return gmm_mx_entry("gmm_mx_w4a8", true, a_u8, a_s, w_u8, w_s, group_list, group_list_type, M, N, Kd, E,
+  return gmm_mx_entry("gmm_mx_w4a8", mxmoe::kWfE2m1, a_u8, a_s, w_u8, w_s, group_list, group_list_type, M, N, Kd, E,
                       y_bf16, stream);
 }
 
@@ -967,7 +984,7 @@ extern "C" int gmm_swiglu_mxquant(const void* a_u8, const void* a_s, const void*
                                   const int64_t* group_list, int group_list_type, int64_t M, int64_t K,
                                   int64_t I, int64_t E, void* hq_u8, void* hs_u8, float* h_f32_debug,
                                   void* stream) {
-  return gmm_swiglu_entry("gmm_swiglu_mxquant", false, a_u8, a_s, w13_u8, w13_s, group_list, group_list_type, M,
+  return gmm_swiglu_entry("gmm_swiglu_mxquant", mxmoe::kWfE4m3, a_u8, a_s, w13_u8, w13_s, group_list, group_list_type, M,
                           K, I, E, hq_u8, hs_u8, h_f32_debug, stream);
 }
 
@@ -975,6 +992,21 @@ extern "C" int gmm_swiglu_mxquant_w4a8(const void* a_u8, const void* a_s, const 
                                        const int64_t* group_list, int group_list_type, int64_t M, int64_t K,
                                        int64_t I, int64_t E, void* hq_u8, void* hs_u8, float* h_f32_debug,
                                        void* stream) {
-  return gmm_swiglu_entry("gmm_swiglu_mxquant_w4a8", true, a_u8, a_s, w13_u8, w13_s, group_list,
+  return gmm_swiglu_entry("gmm_swiglu_mxquant_w4a8", mxmoe::kWfE2m1, a_u8, a_s, w13_u8, w13_s, group_list,
+                          group_list_type, M, K, I, E, hq_u8, hs_u8, h_f32_debug, stream);
+}
+
+extern "C" int gmm_mx_packed(const void* a_u8, const void* a_s, const void* w_packed, const void* w_s,
+                             const int64_t* group_list, int group_list_type, int64_t M, int64_t N, int64_t Kd,
+                             int64_t E, void* y_bf16, void* stream) {
+  return gmm_mx_entry("gmm_mx_packed", mxmoe::kWfPacked, a_u8, a_s, w_packed, w_s, group_list, group_list_type, M,
+                      N, Kd, E, y_bf16, stream);
+}
+
+extern "C" int gmm_swiglu_mxquant_packed(const void* a_u8, const void* a_s, const void* w13_packed,
+                                         const void* w13_s, const int64_t* group_list, int group_list_type,
+                                         int64_t M, int64_t K, int64_t I, int64_t E, void* hq_u8, void* hs_u8,
+                                         float* h_f32_debug, void* stream) {
+  return gmm_swiglu_entry("gmm_swiglu_mxquant_packed", mxmoe::kWfPacked, a_u8, a_s, w13_packed, w13_s, group_list,
                           group_list_type, M, K, I, E, hq_u8, hs_u8, h_f32_debug, stream);
 }

@@ -17,7 +17,7 @@ int launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t kd, int64_t ld, 
 int check_gmm_common(const char* name, int gl_type, int64_t M, int64_t Kd, int64_t E);
 int launch_gmm_mx(const uint8_t* a, const uint8_t* as, const uint8_t* w, const uint8_t* ws, const int64_t* gl,
                   int gl_type, int64_t M, int64_t N, int64_t Kd, int64_t E, uint16_t* y, hipStream_t stream,
-                  bool w4);
+                  int wf);
 
 namespace {
 
@@ -67,5 +67,5 @@ extern "C" int mx_linear(const void* x_bf16, const void* w_u8, const void* w_s, 
   rc = launch_mx_quantize(static_cast<const uint16_t*>(x_bf16), T, K, K, xq, xs, s);
   if (rc) return rc;
   return launch_gmm_mx(xq, xs, static_cast<const uint8_t*>(w_u8), static_cast<const uint8_t*>(w_s), nullptr,
-                       /*single group of T rows*/ 2, T, N, K, 1, static_cast<uint16_t*>(y_bf16), s, false);
+                       /*single group of T rows*/ 2, T, N, K, 1, static_cast<uint16_t*>(y_bf16), s, kWfE4m3);
 }

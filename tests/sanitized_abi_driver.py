@@ -34,6 +34,10 @@ SIG = {
     "moe_router": (I32, [P, P, P, I64, I64, I64, I64, I32, P, P, P]),
     "mx_linear_workspace_size": (SZ, [I64, I64]),
     "mx_linear": (I32, [P, P, P, I64, I64, I64, P, P, SZ, P]),
+    "mx_pack_weights": (I32, [P, I64, I64, I64, I32, P, P]),
+    "gmm_mx_packed": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]),
+    "gmm_swiglu_mxquant_packed": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P, P, P]),
+    "moe_mxfp8_forward_packed": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
     "mx_last_error": (ctypes.c_char_p, []),
 }
 for name, (res, args) in SIG.items():
@@ -111,7 +115,7 @@ for v in NEG + BIG:
     expect(q(64, 2, v), 0, f"route ws query E {v}")
 
 # ---- grouped GEMMs --------------------------------------------------------
-for fn in (lib.gmm_mx, lib.gmm_mx_w4a8):
+for fn in (lib.gmm_mx, lib.gmm_mx_w4a8, lib.gmm_mx_packed):
     def call(M, N, Kd, E, t=1, gl=F, a=F):
         return fn(a, F, F, F, gl, t, M, N, Kd, E, F, None)
     expect(call(64, 256, 256, 4, t=2), INVALID, "gmm group_list_type 2")
@@ -134,7 +138,7 @@ for fn in (lib.gmm_mx, lib.gmm_mx_w4a8):
     expect(call(64, 200, 256, 4), UNSUPPORTED, "gmm N % 256")
     expect(call(64, 256, 256, 1025), UNSUPPORTED, "gmm E > 1024")
     expect(call(64, 256, (1 << 20) + 128, 4), UNSUPPORTED, "gmm Kd past 2^20")
-for fn in (lib.gmm_swiglu_mxquant, lib.gmm_swiglu_mxquant_w4a8):
+for fn in (lib.gmm_swiglu_mxquant, lib.gmm_swiglu_mxquant_w4a8, lib.gmm_swiglu_mxquant_packed):
     def call(M, K, I, E, t=1, hq=F):
         return fn(F, F, F, F, F, t, M, K, I, E, hq, F, None, None)
     expect(call(64, 256, 128, 4, hq=None), INVALID, "gmm1 null hq")
@@ -163,7 +167,7 @@ for v in BIG:
 expect(fz(F, F, F, 4, 60, 2, 8, F, None), UNSUPPORTED, "finalize K % 8")
 
 # ---- forward --------------------------------------------------------------
-for fn in (lib.moe_mxfp8_forward, lib.moe_w4a8_forward):
+for fn in (lib.moe_mxfp8_forward, lib.moe_w4a8_forward, lib.moe_mxfp8_forward_packed):
     def call(T, K, I, E, k, wsb=1 << 40, ws=F, out=F):
         return fn(F, F, F, F, F, F, F, T, K, I, E, k, out, ws, wsb, None)
     expect(call(64, 256, 128, 8, 2, ws=None), INVALID, "forward null workspace")
@@ -191,6 +195,21 @@ for v in NEG + BIG:
         a[i] = v
         expect(fq(*a), 0, f"forward ws query arg {i} = {v}")
         expect(lib.moe_mxfp8_forward_workspace_layout(*a, offs), (INVALID, UNSUPPORTED), f"layout arg {i} = {v}")
+
+# ---- weight packing ---------------------------------------------------------
+pk = lib.mx_pack_weights
+G = ctypes.c_void_p(0x10000000)
+expect(pk(None, 2, 256, 128, 0, G, None), INVALID, "pack null w")
+expect(pk(F, 2, 256, 128, 3, G, None), INVALID, "pack kind")
+for v in NEG:
+    expect(pk(F, v, 256, 128, 0, G, None), INVALID, f"pack E {v}")
+    expect(pk(F, 2, v, 128, 0, G, None), INVALID, f"pack N {v}")
+    expect(pk(F, 2, 256, v, 0, G, None), INVALID, f"pack Kd {v}")
+for v in BIG:
+    expect(pk(F, v, 256, 128, 0, G, None), UNSUPPORTED, f"pack E {v}")
+    expect(pk(F, 2, v // 256 * 256, 128, 1, G, None), UNSUPPORTED, f"pack N {v}")
+    expect(pk(F, 2, 256, v // 128 * 128, 0, G, None), UNSUPPORTED, f"pack Kd {v}")
+expect(pk(F, 2, 256, 128, 0, ctypes.c_void_p(0x1000 + 64), None), INVALID, "pack overlap")
 
 # ---- router ---------------------------------------------------------------
 rt = lib.moe_router

@@ -95,6 +95,22 @@ def test_route_noalloc_validation(lib):
     assert "routing scratch" in mx.last_error()
     assert mx.route_workspace_size(262112, 8, 128) <= 4 << 20 < mx.route_workspace_size(262113, 8, 128)
 
+
+def test_pack_validation(lib):
+    f = lib.mx_pack_weights
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    other = ctypes.c_void_p(0x10000000)
+    assert f(None, 2, 256, 128, 0, other, None) == INVALID
+    assert f(FAKE, 0, 256, 128, 0, other, None) == INVALID
+    assert f(FAKE, 2, 256, 128, 2, other, None) == INVALID          # kind
+    assert f(FAKE, 2, 200, 128, 0, other, None) == UNSUPPORTED      # N % 256
+    assert f(FAKE, 2, 256, 100, 1, other, None) == UNSUPPORTED      # Kd % 128
+    assert f(FAKE, 2000, 256, 128, 0, other, None) == UNSUPPORTED   # E > 1024
+    assert f(FAKE, 2, 256, 128, 0, ctypes.c_void_p(0x1000 + 256 * 128), None) == INVALID   # overlap
+    assert "overlap" in mx.last_error()
+    assert f(ctypes.c_void_p(0x1008), 2, 256, 128, 0, other, None) == UNSUPPORTED          # alignment
+
 def test_gmm_validation(lib):
     g = lib.gmm_mx
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, 256, 128, 4, FAKE, None) == INVALID   # bad type
