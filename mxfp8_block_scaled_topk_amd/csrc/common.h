@@ -102,6 +102,22 @@ __device__ __forceinline__ uint32_t mx_block32(const float (&v)[32], uint32_t (&
   return sb;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active) by DPP
+// data movement, no LDS: shifts by 1, 2, 4 and 8 lanes inside each row of 16
+// lanes (a lane whose source falls outside its row adds 0), then lane 15's
+// running total added to row 1 and lane 47's to row 3 (row_bcast:15 under
+// row mask 0b1010), then lane 31's to rows 2 and 3 (row_bcast:31 under row
+// mask 0b1100).
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+
 // Eight bf16 values packed in a uint4 -> floats.
 __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
   f[0] = __uint_as_float(u.x << 16); f[1] = __uint_as_float(u.x & 0xFFFF0000u);

@@ -84,19 +84,14 @@ __global__ __launch_bounds__(kThreads) void route_scan(int32_t* __restrict__ cou
       v[j] = i0 + j < nchunks ? row[i0 + j] : 0;
       s += v[j];
     }
-    int x = s;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
+    const int x = wave_inclusive_scan(s);
     int excl = run + x - s;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (i0 + j < nchunks) row[i0 + j] = excl;
       excl += v[j];
     }
-    run += __shfl(x, 63);
+    run += __builtin_amdgcn_readlane(x, 63);
   }
   if (lane == 0) {
     totals[e] = run;
@@ -117,12 +112,7 @@ __device__ void block_exclusive_scan(const int32_t* v, int n, int* out, int* s_w
     loc[i] = e < n ? v[e] : 0;
     sum += loc[i];
   }
-  int x = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_inclusive_scan(sum);
   if (lane == 63) s_wsum[wave] = x;
   __syncthreads();
   int base = 0;
