@@ -332,14 +332,17 @@ def profile_workload(name, warmup, steps, dev, copy_calibration):
                       "algorithmic": algorithmic(cfg, counts)}), flush=True)
 
 
-# rocprofv3 kernel names of the layer's kernels -> the step they implement
-_STEP_OF = {"route_hist": "route_quant", "route_scan": "route_quant", "route_scatter_quant": "route_quant",
-            "gmm_kernel<true, false, 4, 256>": "gemm1_swiglu_requant",
-            "gmm_kernel<true, false, 1, 256>": "gemm1_swiglu_requant",
-            "gmm_kernel<true, false, 1, 128>": "gemm1_swiglu_requant",
-            "gmm_kernel<false, false, 4, 256>": "gemm2", "gmm_kernel<false, false, 1, 256>": "gemm2",
-            "gmm_kernel<false, false, 1, 128>": "gemm2",
-            "finalize_kernel<true>": "finalize", "finalize_kernel<false>": "finalize"}
+def _step_of(kernel):
+    """The layer step a rocprofv3 kernel name belongs to (None: not a layer kernel)."""
+    if kernel in ("route_hist", "route_scan", "route_scatter_quant"):
+        return "route_quant"
+    if kernel.startswith("gmm_kernel<true"):
+        return "gemm1_swiglu_requant"
+    if kernel.startswith("gmm_kernel<false"):
+        return "gemm2"
+    if kernel.startswith("finalize_kernel"):
+        return "finalize"
+    return None
 
 
 def counter_summary(name, fetch_dir, write_dir, sq_dir, tcc_dir):
@@ -381,9 +384,9 @@ def counter_summary(name, fetch_dir, write_dir, sq_dir, tcc_dir):
              "ratio | clock GHz | MFMA busy | LDS bank conflict | L2 hit rate |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for k in fe:
-        if k.startswith("__amd") or k not in _STEP_OF:
+        st = _step_of(k)
+        if st is None:
             continue
-        st = _STEP_OF[k]
         rd = np.mean([e["FETCH_SIZE"] for e in fe[k]]) * 1024 * ff / 1e6
         wt = np.mean([e["WRITE_SIZE"] for e in wr[k]]) * 1024 * fw / 1e6
         S = sq[k]
