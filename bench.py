@@ -59,8 +59,8 @@ AUX_WARMUP = 50
 # a 1 GiB device-to-device copy in the same run (--copy-calibration).  Valid
 # only for the kernel they were taken on: the SHA-256 of csrc/gmm.hip is
 # checked at run time and the traffic is reported as null on a mismatch.
-GEMM1_TRAFFIC = {"gmm_sha256": "71c49c010d697e8d23c9546659225981050530b42bf10a28b6c7e3ff5276ae09",
-                 "fetch_bytes": 1.26140e+09, "write_bytes": 1.05201e+08}
+GEMM1_TRAFFIC = {"gmm_sha256": "6139f7167727c05f0a1e1d97a33f422f7e7eb719ce8cef940e9f4147eb8ca238",
+                 "fetch_bytes": 1.2688e+09, "write_bytes": 1.053e+08}
 
 
 def gemm1_traffic():
@@ -332,47 +332,106 @@ def profile_workload(name, warmup, steps, dev, copy_calibration):
                       "algorithmic": algorithmic(cfg, counts)}), flush=True)
 
 
-def _step_of(kernel):
-    """The layer step a rocprofv3 kernel name belongs to (None: not a layer kernel)."""
+def _step_of(kernel, bench_run=False):
+    """The layer step a rocprofv3 kernel name belongs to (None: not a layer
+    kernel).  In bench.py's default run (`bench_run`) the 16K prefill layer's
+    GEMM2 is the per-stage-scale instance (I = 768 is 6 k stages) and the
+    4-stage-group instance is the dense linear's GEMM."""
     if kernel in ("route_hist", "route_scan", "route_scatter_quant"):
         return "route_quant"
-    if kernel.startswith("gmm_kernel<true"):
+    if kernel.startswith("gmm_kernel<true, 0") or kernel.startswith("gmm_kernel<true, 2"):
         return "gemm1_swiglu_requant"
-    if kernel.startswith("gmm_kernel<false"):
+    if kernel.startswith("gmm_kernel<false, 0") or kernel.startswith("gmm_kernel<false, 2"):
+        if bench_run and kernel.startswith("gmm_kernel<false, 0, 4"):
+            return None
         return "gemm2"
     if kernel.startswith("finalize_kernel"):
         return "finalize"
     return None
 
 
-def counter_summary(name, fetch_dir, write_dir, sq_dir, tcc_dir):
-    """--counter-summary: markdown tables from four rocprofv3 --pmc runs of
-    `--profile-workload name --copy-calibration` (FETCH_SIZE; WRITE_SIZE;
-    SQ and GRBM counters; TCC hit/miss), per kernel: HBM bytes per dispatch
-    calibrated on the 1 GiB copies, against the kernel's algorithmic bytes;
-    shader clock; MFMA busy; LDS bank conflicts; L2 hit rate."""
+def _aux_algorithmic(cfg):
+    """Algorithmic bytes of the kernels bench.py's default run times outside
+    the layer's step (shapes as in main())."""
+    T, K, I, E, k = cfg.T, cfg.K, cfg.I, cfg.E, cfg.k
+    M = T * k
+    LT, LK, LN = 16384, 4096, 4096
+    R = E * 2 * I
+    return {
+        "router": 2 * T * K + 2 * E * K + 8 * T * k,
+        "dense linear GEMM": LT * LK * (1 + 1 / 32) + LN * LK * (1 + 1 / 32) + 2 * LT * LN,
+        "dense linear activation quant": 2 * LT * LK + LT * LK * (1 + 1 / 32),
+        "weight quant e4m3": R * K * (2 + 1 + 1 / 32),
+        "weight quant e2m1": R * K * (2 + 1 / 2 + 1 / 32),
+        "W4A8 GEMM1": M * K * (1 + 1 / 32) + E * 2 * I * K * (1 / 2 + 1 / 32) + M * I * (1 + 1 / 32),
+        "W4A8 GEMM2": M * I * (1 + 1 / 32) + E * K * I * (1 / 2 + 1 / 32) + 2 * M * K,
+    }
+
+
+def _aux_role(kernel, dur_us):
+    """Which outside-the-step workload a kernel dispatch of the default run is."""
+    if kernel.startswith("router_kernel"):
+        return "router"
+    if kernel.startswith("gmm_kernel<false, 0, 4"):
+        return "dense linear GEMM"
+    if kernel == "mx_quantize_vec":
+        # the same kernel quantises the dense linear's activations (16384 x 4096,
+        # about 30 us) and w13-shaped weights (196608 x 2048, about 225 us)
+        return "dense linear activation quant" if dur_us < 100 else "weight quant e4m3"
+    if kernel.startswith("mx_quantize_fp4_kernel"):
+        return "weight quant e2m1"
+    if kernel.startswith("gmm_kernel<true, 1"):
+        return "W4A8 GEMM1"
+    if kernel.startswith("gmm_kernel<false, 1"):
+        return "W4A8 GEMM2"
+    return None
+
+
+def _load_rocprof_csv(d, pattern):
     import csv
     import glob
     import re
+    path = glob.glob(os.path.join(d, "**", pattern), recursive=True)[0]
+    rows = list(csv.DictReader(open(path)))
 
+    def short(n):
+        return re.sub(r"\(.*$", "", n.replace("void ", "").replace("mxmoe::(anonymous namespace)::", ""))
+    return rows, short
+
+
+def counter_summary(name, fetch_dir, write_dir, sq_dir, tcc_dir):
+    """--counter-summary: markdown table from four rocprofv3 --pmc runs
+    (FETCH_SIZE; WRITE_SIZE; SQ and GRBM counters; TCC hit/miss) of
+    `--profile-workload name --copy-calibration`, or with name "bench" of the
+    default run without the per-workload table (`--no-workloads
+    --no-cpu-baseline --copy-calibration`, where the kernels outside the step
+    get rows of their own).  Per kernel (and role): HBM bytes per dispatch
+    calibrated on the 1 GiB copies, against the algorithmic bytes of its step;
+    shader clock; MFMA busy; LDS bank conflicts; L2 hit rate."""
     def load(d):
-        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        rows, short = _load_rocprof_csv(d, "*counter_collection.csv")
         disp = {}
-        for r in csv.DictReader(open(path)):
-            n = re.sub(r"\(.*$", "", r["Kernel_Name"].replace("void ", "").replace(
-                "mxmoe::(anonymous namespace)::", ""))
+        for r in rows:
+            n = short(r["Kernel_Name"])
             e = disp.setdefault(r["Dispatch_Id"], {"name": n, "dur_us": (int(r["End_Timestamp"]) -
                                                                           int(r["Start_Timestamp"])) / 1e3})
             e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         per = {}
         for e in disp.values():
-            per.setdefault(e["name"], []).append(e)
+            if name == "bench" and _step_of(e["name"], True) is None:
+                role = _aux_role(e["name"], e["dur_us"])
+                key = f"{e['name']} ({role})" if role else e["name"]
+            else:
+                key = e["name"]
+            per.setdefault(key, []).append(e)
         return per
 
-    cfg = CONFIGS[name]
+    cfg = CONFIGS["prefill" if name == "bench" else name]
     d = make_inputs(cfg, weights=False)
     counts = np.bincount(d["topk_ids"].reshape(-1), minlength=cfg.E)
-    alg = algorithmic(cfg, counts)
+    alg = {st: a["bytes"] for st, a in algorithmic(cfg, counts).items()}
+    if name == "bench":
+        alg.update(_aux_algorithmic(cfg))
     fe, wr, sq, tc = load(fetch_dir), load(write_dir), load(sq_dir), load(tcc_dir)
     cf = [e["FETCH_SIZE"] for e in fe.get("__amd_rocclr_copyBuffer", []) if e["FETCH_SIZE"] > 1e5]
     cw = [e["WRITE_SIZE"] for e in wr.get("__amd_rocclr_copyBuffer", []) if e["WRITE_SIZE"] > 1e5]
@@ -380,12 +439,15 @@ def counter_summary(name, fetch_dir, write_dir, sq_dir, tcc_dir):
     lines = [f"Calibration: {len(cf)} copies of 1 GiB; FETCH_SIZE reads {np.mean(cf):.0f} KiB and WRITE_SIZE "
              f"{np.mean(cw):.0f} KiB per copy, so bytes = FETCH_SIZE x 1024 x {ff:.4f} and WRITE_SIZE x 1024 x "
              f"{fw:.4f}.", "",
-             "| kernel | step | dispatches | avg µs | read MB | written MB | total MB | algorithmic MB (step) | "
+             "| kernel | step / role | dispatches | avg µs | read MB | written MB | total MB | algorithmic MB | "
              "ratio | clock GHz | MFMA busy | LDS bank conflict | L2 hit rate |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for k in fe:
-        st = _step_of(k)
-        if st is None:
+        if k.startswith("__amd") or k.startswith("at::") or k not in sq or k not in tc or k not in wr:
+            continue
+        base = k.split(" (")[0]
+        st = _step_of(base, name == "bench") or (k[len(base) + 2:-1] if " (" in k else None)
+        if st is None or st not in alg:
             continue
         rd = np.mean([e["FETCH_SIZE"] for e in fe[k]]) * 1024 * ff / 1e6
         wt = np.mean([e["WRITE_SIZE"] for e in wr[k]]) * 1024 * fw / 1e6
@@ -397,11 +459,28 @@ def counter_summary(name, fetch_dir, write_dir, sq_dir, tcc_dir):
         lds = sum(e["SQ_LDS_BANK_CONFLICT"] for e in S) / max(1.0, sum(e["SQ_LDS_IDX_ACTIVE"] for e in S))
         hit = sum(e["TCC_HIT_sum"] for e in tc[k])
         miss = sum(e["TCC_MISS_sum"] for e in tc[k])
-        a = alg[st]["bytes"] / 1e6
-        ratio = f"{(rd + wt) / a:.2f}" if k not in ("route_hist", "route_scan") else ""
-        lines.append(f"| {k} | {st} | {len(fe[k])} | {dur:.1f} | {rd:.1f} | {wt:.1f} | {rd + wt:.1f} | {a:.1f} | "
-                     f"{ratio} | {clk:.2f} | {mf:.3f} | {lds:.3f} | {hit / max(1.0, hit + miss):.3f} |")
+        a = alg[st] / 1e6
+        ratio = f"{(rd + wt) / a:.2f}" if base not in ("route_hist", "route_scan") else ""
+        clock = f"{clk:.2f}" if dur >= 20 else ""     # GRBM_GUI_ACTIVE spans more than a short kernel
+        lines.append(f"| {base} | {st} | {len(fe[k])} | {dur:.1f} | {rd:.1f} | {wt:.1f} | {rd + wt:.1f} | {a:.1f} | "
+                     f"{ratio} | {clock} | {mf:.3f} | {lds:.3f} | {hit / max(1.0, hit + miss):.3f} |")
     print("\n".join(lines))
+
+
+def trace_summary(trace_dir, last=50):
+    """--trace-summary: per kernel, from a rocprofv3 --kernel-trace run: calls,
+    average over all calls and over the last `last` calls, min, max (µs)."""
+    rows, short = _load_rocprof_csv(trace_dir, "*kernel_trace.csv")
+    per = {}
+    for r in sorted(rows, key=lambda r: int(r["Start_Timestamp"])):
+        n = short(r["Kernel_Name"])
+        if n.startswith("at::"):
+            continue
+        per.setdefault(n, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"| kernel | calls | avg µs (all calls) | avg µs (last {last} calls) | min µs | max µs |")
+    print("|---|---|---|---|---|---|")
+    for n, v in per.items():
+        print(f"| {n} | {len(v)} | {np.mean(v):.1f} | {np.mean(v[-last:]):.1f} | {min(v):.1f} | {max(v):.1f} |")
 
 
 def main():
@@ -420,10 +499,16 @@ def main():
     ap.add_argument("--profile-workload", choices=list(CONFIGS),
                     help="only run this workload's layer (--warmup + --steps steps), for counter runs")
     ap.add_argument("--counter-summary", nargs=5, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "SQ_DIR", "TCC_DIR"),
-                    help="print counter tables from four rocprofv3 --pmc runs of --profile-workload (no GPU)")
+                    help="print counter tables from four rocprofv3 --pmc runs of --profile-workload WORKLOAD, or "
+                         "of the default run when WORKLOAD is 'bench' (no GPU needed)")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="print per-kernel durations from a rocprofv3 --kernel-trace run (no GPU needed)")
     args = ap.parse_args()
     if args.counter_summary:
         counter_summary(*args.counter_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: the layer is measured on one GPU only (one GPU holds all experts; "
