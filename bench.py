@@ -337,7 +337,7 @@ def _step_of(kernel, bench_run=False):
     kernel).  In bench.py's default run (`bench_run`) the 16K prefill layer's
     GEMM2 is the per-stage-scale instance (I = 768 is 6 k stages) and the
     4-stage-group instance is the dense linear's GEMM."""
-    if kernel in ("route_hist", "route_scan", "route_scatter_quant"):
+    if kernel.startswith("route_quant_kernel"):
         return "route_quant"
     if kernel.startswith("gmm_kernel<true, 0") or kernel.startswith("gmm_kernel<true, 2"):
         return "gemm1_swiglu_requant"
@@ -460,7 +460,7 @@ def counter_summary(name, fetch_dir, write_dir, sq_dir, tcc_dir):
         hit = sum(e["TCC_HIT_sum"] for e in tc[k])
         miss = sum(e["TCC_MISS_sum"] for e in tc[k])
         a = alg[st] / 1e6
-        ratio = f"{(rd + wt) / a:.2f}" if base not in ("route_hist", "route_scan") else ""
+        ratio = f"{(rd + wt) / a:.2f}"
         clock = f"{clk:.2f}" if dur >= 20 else ""     # GRBM_GUI_ACTIVE spans more than a short kernel
         lines.append(f"| {base} | {st} | {len(fe[k])} | {dur:.1f} | {rd:.1f} | {wt:.1f} | {rd + wt:.1f} | {a:.1f} | "
                      f"{ratio} | {clock} | {mf:.3f} | {lds:.3f} | {hit / max(1.0, hit + miss):.3f} |")

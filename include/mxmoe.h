@@ -78,12 +78,13 @@
  * group lists are clamped to [0, M] rows.
  *
  * GPU shape limits (MX_ERR_UNSUPPORTED otherwise): every size argument at
- * most 2^31 - 1, and M = T*k below 2^31; GEMM reduction dims (K of GEMM1,
+ * most 2^31 - 1, and M = T*k at most 2^27 for routing and the layer (below
+ * 2^31 for the GEMMs and finalize); GEMM reduction dims (K of GEMM1,
  * I of GEMM2) multiples of 128 and at most 2^20; GEMM2 output dim N a
  * multiple of 256;
  * GEMM1 intermediate size I a multiple of 128 (so the forward needs K % 256
- * == 0 and I % 128 == 0); routing needs K % 32 == 0, 1 <= k <= 256 and
- * E <= 1024; mx_quantize takes any Kd >= 1.
+ * == 0 and I % 128 == 0); routing needs K % 32 == 0, K <= 2^24,
+ * 1 <= k <= 256 and E <= 1024; mx_quantize takes any Kd >= 1.
  *
  * Alignment (MX_ERR_UNSUPPORTED otherwise): e4m3 payload and bf16 tensors
  * that the GEMMs, routing and finalize read or write (x, xq, a, w, w13, w2,
@@ -134,7 +135,8 @@ int mx_quantize(const void* x_bf16, int64_t rows, int64_t kd, int64_t ld,
 int mx_quantize_fp4(const void* x_bf16, int64_t rows, int64_t kd, int64_t ld,
                     void* q_u8, void* s_u8, void* stream);
 
-/* Workspace bytes moe_route_quant needs for T tokens, top-k, E experts. */
+/* Workspace bytes moe_route_quant needs for T tokens, top-k, E experts
+ * (0 when T*k <= 256: the call then accepts a null workspace). */
 size_t moe_route_quant_workspace_size(int64_t T, int64_t k, int64_t E);
 
 /*
@@ -148,6 +150,12 @@ size_t moe_route_quant_workspace_size(int64_t T, int64_t k, int64_t E);
  *   expanded_row_idx  int32 [M]           row p of flat assignment i (-1 if its id was invalid)
  *   group_list        int64 [E]           rows per expert (count form, type 1)
  * Rows past sum(group_list) (only when ids were invalid) are left unwritten.
+ * One kernel launch.  Its workgroups exchange per-chunk expert counts through
+ * the workspace under flags tagged per call, so the workspace needs no
+ * clearing; a workgroup that finds the counts not yet published after a
+ * bounded number of polls (moe_route_quant_set_wait_limit) counts them from
+ * topk_ids itself, so the call always ends and its output never depends on
+ * the order the GPU runs the workgroups in.
  */
 int moe_route_quant(const void* x_bf16, const int32_t* topk_ids,
                     int64_t T, int64_t K, int64_t k, int64_t E,
@@ -159,23 +167,33 @@ int moe_route_quant(const void* x_bf16, const int32_t* topk_ids,
  * moe_route_quant for callers that cannot allocate: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
  * arguments, outputs and results as moe_route_quant minus the workspace:
- * the routing scratch (per-chunk expert counts and the experts' totals) is
- * a 4 MiB device array inside the library, one per GPU, held until the
+ * the routing scratch (per-chunk expert counts, the experts' offsets and
+ * the flags that publish them) is a 4 MiB device array inside the library, one per GPU, held until the
  * process ends.  The call allocates nothing (no hipMalloc, hipFree or
  * allocating library routine); the caller still passes every input and
  * output.  Sizes whose scratch, moe_route_quant_workspace_size(T, k, E),
  * exceeds 4 MiB (4,194,304 bytes) are rejected with MX_ERR_UNSUPPORTED
- * before anything is enqueued (e.g. E = 128, k = 8: up to 262,112 tokens).
+ * before anything is enqueued (e.g. E = 128, k = 8: up to 261,088 tokens).
  * Every call on one GPU shares that GPU's array: calls that overlap in time
  * on one GPU (other streams, other host threads) race and must not be
  * issued; calls ordered on one stream are safe.  The array needs no
- * clearing: each call writes every element it reads before reading it.
+ * clearing: each call writes every count it reads before reading it, and
+ * its flags match only the tag of the call that set them.
  */
 int moe_route_quant_noalloc(const void* x_bf16, const int32_t* topk_ids,
                             int64_t T, int64_t K, int64_t k, int64_t E,
                             void* xq_u8, void* xs_u8, int32_t* sorted_row,
                             int32_t* expanded_row_idx, int64_t* group_list,
                             void* stream);
+
+/*
+ * How many times a routing workgroup polls for the published expert counts
+ * before counting them from topk_ids itself (process-wide, default 2^18;
+ * 0 makes every workgroup count for itself: much slower, same output).
+ * Applies to launches enqueued after the call; returns the previous value.
+ * Negative values are taken as 0.  Meant for tests of that path.
+ */
+int64_t moe_route_quant_set_wait_limit(int64_t polls);
 
 /*
  * Grouped GEMM1 with SwiGLU and MX requant fused ("Quantization on Ascend",

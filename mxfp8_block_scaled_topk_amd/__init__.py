@@ -23,7 +23,7 @@ __all__ = [
     "MxError", "lib_path", "load", "mx_quantize", "moe_route_quant", "gmm_swiglu_mxquant",
     "gmm_mx", "moe_finalize", "moe_mxfp8_forward", "forward_workspace", "forward_intermediates",
     "route_workspace_size", "forward_workspace_size", "last_error", "moe_router", "mx_linear",
-    "linear_workspace_size", "mx_quantize_fp4", "moe_route_quant_noalloc", "mx_pack_weights",
+    "linear_workspace_size", "mx_quantize_fp4", "moe_route_quant_noalloc", "mx_pack_weights", "route_set_wait_limit",
     "gmm_swiglu_mxquant_packed", "gmm_mx_packed", "moe_mxfp8_forward_packed", "gmm_mx_w4a8", "gmm_swiglu_mxquant_w4a8", "moe_w4a8_forward",
 ]
 
@@ -61,6 +61,7 @@ def load():
         "moe_route_quant_workspace_size": (SZ, [I64, I64, I64]),
         "moe_route_quant": (I32, [P, P, I64, I64, I64, I64, P, P, P, P, P, P, SZ, P]),
         "moe_route_quant_noalloc": (I32, [P, P, I64, I64, I64, I64, P, P, P, P, P, P]),
+        "moe_route_quant_set_wait_limit": (I64, [I64]),
         "gmm_swiglu_mxquant": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P, P, P]),
         "gmm_mx": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]),
         "gmm_mx_w4a8": (I32, [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]),
@@ -196,6 +197,13 @@ def mx_quantize(x, q=None, s=None, stream=None):
 
 def route_workspace_size(T, k, E):
     return int(load().moe_route_quant_workspace_size(T, k, E))
+
+
+def route_set_wait_limit(polls):
+    """Polls a routing workgroup makes for the published expert counts before
+    counting them itself (process-wide; 0 = always count). Returns the
+    previous value."""
+    return int(load().moe_route_quant_set_wait_limit(int(polls)))
 
 
 @_stream_scoped

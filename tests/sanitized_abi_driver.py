@@ -102,13 +102,15 @@ for fn, ws in ((lib.moe_route_quant, True), (lib.moe_route_quant_noalloc, False)
     expect(call(64, 100, 2, 8), UNSUPPORTED, "route K % 32")
     expect(call(64, 256, 300, 400), UNSUPPORTED, "route k > 256")
     expect(call((1 << 31) // 8, 256, 8, 16), UNSUPPORTED, "route T*k = 2^31")
+    expect(call((1 << 27) // 8 + 1, 256, 8, 16), UNSUPPORTED, "route T*k above 2^27")
     if ws:
-        expect(call(64, 256, 2, 8, wsb=0), WORKSPACE, "route workspace 0")
+        expect(call(300, 256, 2, 8, wsb=0), WORKSPACE, "route workspace 0")
     else:
         expect(call(32768, 256, 8, 1024), UNSUPPORTED, "noalloc past its scratch")
         assert "routing scratch" in err()
 q = lib.moe_route_quant_workspace_size
-expect(q(64, 2, 8) > 0, True, "route ws query valid")
+expect(q(300, 2, 8) > 0, True, "route ws query valid")
+expect(q(128, 2, 8), 0, "route ws query one chunk")
 for v in NEG + BIG:
     expect(q(v, 2, 8), 0, f"route ws query T {v}")
     expect(q(64, v, 8), 0, f"route ws query k {v}")

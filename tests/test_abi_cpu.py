@@ -71,7 +71,7 @@ def test_route_validation(lib):
     assert args(64, 100, 2, 8) == UNSUPPORTED      # K % 32
     assert args(64, 256, 2, 2048) == UNSUPPORTED   # E > 1024
     assert args(64, 256, 300, 400) == UNSUPPORTED  # k > 256
-    assert args(64, 256, 2, 8, ws=0) == WORKSPACE
+    assert args(300, 256, 2, 8, ws=0) == WORKSPACE   # 600 assignments: 3 routing chunks
     assert "workspace" in mx.last_error()
     assert f(None, FAKE, 64, 256, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
 
@@ -88,12 +88,12 @@ def test_route_noalloc_validation(lib):
     assert args(64, 256, 2, 2048) == UNSUPPORTED
     assert f(None, FAKE, 64, 256, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
     assert f(FAKE, FAKE, 64, 256, 2, 8, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
-    # E = 1024, top-8: 1024 routing chunks (32768 tokens) need 4 MiB of counts plus the totals
-    assert mx.route_workspace_size(32768, 8, 1024) > 4 << 20
-    assert mx.route_workspace_size(32768 - 32, 8, 1024) <= 4 << 20
-    assert args(32768, 256, 8, 1024) == UNSUPPORTED
+    # E = 1024, top-8: 4 KB of counts per 32-token routing chunk, plus the
+    # super-chunk offsets (128 KB) and flags: 991 chunks fit in 4 MiB
+    assert mx.route_workspace_size(31712, 8, 1024) <= 4 << 20 < mx.route_workspace_size(31713, 8, 1024)
+    assert args(31713, 256, 8, 1024) == UNSUPPORTED
     assert "routing scratch" in mx.last_error()
-    assert mx.route_workspace_size(262112, 8, 128) <= 4 << 20 < mx.route_workspace_size(262113, 8, 128)
+    assert mx.route_workspace_size(261088, 8, 128) <= 4 << 20 < mx.route_workspace_size(261089, 8, 128)
 
 
 def test_pack_validation(lib):
@@ -226,7 +226,9 @@ def test_binding_route_finalize_forward_shape_checks(lib):
     _raises(lambda: mx.moe_route_quant(x, ids, E, out=(_u8(T * k, K), _u8(T * k, 3, 2), ids.flatten(),
                                                        ids.flatten(), torch.zeros(E, dtype=torch.int64))),
             "xs must have shape")
-    _raises(lambda: mx.moe_route_quant(x, ids, E, workspace=_u8(1)), "workspace has 1 bytes")
+    # 300 tokens x top-2: three routing chunks, so a workspace is needed
+    x3, ids3 = torch.zeros(300, K, dtype=torch.bfloat16), torch.zeros(300, k, dtype=torch.int32)
+    _raises(lambda: mx.moe_route_quant(x3, ids3, E, workspace=_u8(1)), "workspace has 1 bytes")
     y = torch.zeros(T * k, K, dtype=torch.bfloat16)
     tw = torch.zeros(T, k, dtype=torch.float32)
     _raises(lambda: mx.moe_finalize(y, tw, ids.flatten()), "on the GPU")

@@ -125,12 +125,17 @@ ROUTE_CASES = {
     "E1": (33, 64, 1, 1, None),
     "k-eq-E": (50, 64, 6, 6, None),
     "big-k": (70, 64, 32, 40, None),
-    # T*k <= 256 is one routing chunk (no histogram/scan launches): the
-    # boundary on both sides, and the largest expert count in one chunk
+    # T*k <= 256 is one routing chunk (no leader workgroups): the boundary on
+    # both sides, and the largest expert count in one chunk
     "one-chunk-full": (32, 256, 8, 128, None),
     "two-chunks-min": (33, 256, 8, 128, None),
     "one-chunk-E1024": (16, 64, 8, 1024, None),
     "one-chunk-hot": (60, 128, 4, 9, "hot"),
+    # leaders owning several chunks each (157 chunks over 32 leaders), in
+    # batches of 3 chunks (E = 1024 fills the LDS counts); 79 chunks of 256
+    # single-expert assignments, the last one ragged
+    "leader-batches-E1024": (5000, 64, 8, 1024, None),
+    "leaders-k1": (20000, 32, 1, 7, None),
 }
 
 
@@ -158,6 +163,49 @@ def test_route_quant_bitexact(name):
     assert np.array_equal(host(eri), reri)
     assert np.array_equal(host(xq), rq)
     assert np.array_equal(host(xs), rs)
+
+
+@pytest.mark.parametrize("limit", [0, 1, 3])
+@pytest.mark.parametrize("name", ["ragged-many-chunks", "hot-many-chunks", "leader-batches-E1024", "leaders-k1"])
+def test_route_quant_wait_paths(name, limit):
+    """A routing workgroup that stops waiting for the published counts counts
+    them from topk_ids itself.  Limit 0 puts every workgroup on that path;
+    1 and 3 polls leave some on each path.  Output bit-exact either way."""
+    T, K, k, E, kind = ROUTE_CASES.get(name) or (1500, 128, 8, 64, "hot")
+    say(f"moe_route_quant {name} T={T} K={K} k={k} E={E} wait limit {limit}")
+    x = _rand_bf16((T, K), scale_spread=10)
+    ids = _route_ids(T, k, E, kind)
+    prev = mx.route_set_wait_limit(limit)
+    try:
+        xq, xs, sr, eri, gl = mx.moe_route_quant(bf16_dev(x), i32_dev(ids), E)
+        torch.cuda.synchronize()
+    finally:
+        mx.route_set_wait_limit(prev)
+    rq, rs, rsr, reri, rc = moe_ref.route_quant_ref(x, ids, E)
+    assert np.array_equal(host(gl), rc)
+    assert np.array_equal(host(sr), rsr)
+    assert np.array_equal(host(eri), reri)
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(xs), rs)
+
+
+def test_route_quant_reused_workspace():
+    """Consecutive calls on one workspace: the second call's flags, counts and
+    offsets replace the first's (its tags differ), never mix with them."""
+    T, K, k, E = 3000, 64, 8, 96
+    ws = torch.empty(mx.route_workspace_size(T, k, E), dtype=torch.uint8, device="cuda")
+    for i, kind in enumerate([None, "hot", None]):
+        say(f"moe_route_quant reused workspace, call {i}")
+        x = _rand_bf16((T, K))
+        ids = _route_ids(T, k, E, kind)
+        xq, xs, sr, eri, gl = mx.moe_route_quant(bf16_dev(x), i32_dev(ids), E, workspace=ws)
+        torch.cuda.synchronize()
+        rq, rs, rsr, reri, rc = moe_ref.route_quant_ref(x, ids, E)
+        assert np.array_equal(host(gl), rc)
+        assert np.array_equal(host(sr), rsr)
+        assert np.array_equal(host(eri), reri)
+        assert np.array_equal(host(xq), rq)
+        assert np.array_equal(host(xs), rs)
 
 
 def test_route_quant_empty_batch():

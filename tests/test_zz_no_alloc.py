@@ -48,15 +48,16 @@ def test_noalloc_matches_workspace_entry_point(sizes):
 
 
 def test_noalloc_rejects_sizes_beyond_its_scratch():
-    # E = 1024, top-8: 32 tokens per routing chunk, 4 KB of counts per chunk;
-    # 1024 chunks need 4 MiB + the totals, past the 4 MiB the library holds
-    T, K, k, E = 32768, 32, 8, 1024
+    # E = 1024, top-8: 32 tokens per routing chunk, 4 KB of counts per chunk,
+    # plus the super-chunk offsets and flags: past 31712 tokens the scratch
+    # needs more than the 4 MiB the library holds
+    T, K, k, E = 31713, 32, 8, 1024
     x = torch.zeros((T, K), dtype=torch.bfloat16, device="cuda")
     ids = torch.zeros((T, k), dtype=torch.int32, device="cuda")
     with pytest.raises(mx.MxError, match="routing scratch"):
         mx.moe_route_quant_noalloc(x, ids, E)
-    # one chunk fewer fits
-    T = 32768 - 32
+    # the largest batch that fits
+    T = 31712
     x, ids = _inputs(T, K, k, E, seed=7)
     say(f"moe_route_quant_noalloc at its limit: T={T} k={k} E={E}")
     got = mx.moe_route_quant_noalloc(x, ids, E)
