@@ -67,6 +67,9 @@ constexpr int kXBufBytes = 40 << 10;
 // scatter workgroups wanted per compute unit (a chunk is split into more
 // shares until the grid has that many)
 constexpr int kScatterPerCU = 4;
+// shares of a single-chunk batch (decode sizes) unless the LDS budget needs
+// more (such calls are launch-bound: 16 or 32 shares time the same)
+constexpr int kSingleShares = 16;
 
 struct RouteParams {
   const uint16_t* x;
@@ -596,10 +599,11 @@ int launch_route_quant(const uint16_t* x, const int32_t* ids, int64_t T, int64_t
   p.S = (int)sp.S;
   // shares per chunk: doubled until a share's quantised rows fit the LDS
   // budget and the grid has kScatterPerCU workgroups per compute unit (at
-  // most one token per share)
+  // most one token per share); a batch of one chunk (nothing to wait for)
+  // takes at most kSingleShares
   const int64_t nb = K / 32, s_stride = ((nb + 1) / 2) * 2;
   const int64_t row_bytes = (int64_t)align_up((size_t)(K + s_stride), 16);
-  const int64_t want = (int64_t)num_cus() * kScatterPerCU;
+  const int64_t want = sp.S == 0 ? kSingleShares : (int64_t)num_cus() * kScatterPerCU;
   int64_t split = 1;
   while (split < sp.tpc &&
          (((sp.tpc + split - 1) / split) * row_bytes > kXBufBytes || sp.nch * split < want))
