@@ -155,7 +155,10 @@ size_t moe_route_quant_workspace_size(int64_t T, int64_t k, int64_t E);
  * clearing; a workgroup that finds the counts not yet published after a
  * bounded number of polls (moe_route_quant_set_wait_limit) counts them from
  * topk_ids itself, so the call always ends and its output never depends on
- * the order the GPU runs the workgroups in.
+ * the order the GPU runs the workgroups in.  Called while `stream` is
+ * capturing, the call also records a one-thread kernel ahead of the routing
+ * kernel that advances a generation word in the workspace, so that every
+ * replay of the captured graph tags its flags afresh.
  */
 int moe_route_quant(const void* x_bf16, const int32_t* topk_ids,
                     int64_t T, int64_t K, int64_t k, int64_t E,
@@ -173,7 +176,7 @@ int moe_route_quant(const void* x_bf16, const int32_t* topk_ids,
  * allocating library routine); the caller still passes every input and
  * output.  Sizes whose scratch, moe_route_quant_workspace_size(T, k, E),
  * exceeds 4 MiB (4,194,304 bytes) are rejected with MX_ERR_UNSUPPORTED
- * before anything is enqueued (e.g. E = 128, k = 8: up to 261,088 tokens).
+ * before anything is enqueued (e.g. E = 128, k = 8: up to 261,056 tokens).
  * Every call on one GPU shares that GPU's array: calls that overlap in time
  * on one GPU (other streams, other host threads) race and must not be
  * issued; calls ordered on one stream are safe.  The array needs no

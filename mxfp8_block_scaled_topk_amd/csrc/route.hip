@@ -62,6 +62,8 @@ constexpr int kThreads = 256;
 constexpr int kMaxE = 1024;
 // most leader blocks (super-chunks) per call
 constexpr int kMaxLeaders = 32;
+// the routing workspace's control block: the 64-bit generation word
+constexpr size_t kCtrlBytes = 256;
 // LDS a scatter workgroup may fill with its share's quantised rows
 constexpr int kXBufBytes = 40 << 10;
 // scatter workgroups wanted per compute unit (a chunk is split into more
@@ -82,7 +84,8 @@ struct RouteParams {
   int32_t* chunk_pre;   // [nch][E] count prefix over the super-chunk's earlier chunks
   int32_t* super;       // [S][E] super-chunk totals per expert
   uint64_t* flags;      // [S + 1]: one per leader, then the ready flag
-  uint64_t tag;         // unique to the call
+  const uint64_t* gen;  // the workspace's generation word (see call_tag)
+  uint64_t tag;         // unique to the host call (the flags' tag mixes in *gen)
   int64_t wait_limit;   // polls before a block counts for itself
   int64_t T, K;
   int k, E, nbits, tpc, nch, G, S;
@@ -153,6 +156,15 @@ __device__ __forceinline__ void store_coherent(int32_t* q, int v) {
   __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The tag this launch's flags carry: the host call's tag mixed with the
+// workspace's generation word.  A call made under stream capture records a
+// kernel that advances the generation before the routing kernel, so every
+// replay of the captured work has its own tag although its arguments, the
+// host tag included, are the captured ones.
+__device__ __forceinline__ uint64_t call_tag(const RouteParams& p, uint64_t gen) {
+  return p.tag ^ (gen * 0x9E3779B97F4A7C15ull);
+}
+
 // Publishes the block's earlier device-scope stores under flag *f.
 __device__ void publish(uint64_t* f, uint64_t tag) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt not waited for
@@ -179,7 +191,7 @@ __device__ void count_all(const RouteParams& p, int64_t before, int* tot, int* p
 }
 
 // Leader of super-chunk s: chunks [s*G, min((s+1)*G, nch)).
-__device__ void leader(const RouteParams& p, int s, int* smem, int lds_ints) {
+__device__ void leader(const RouteParams& p, int s, int* smem, int lds_ints, uint64_t tag) {
   const int tid = threadIdx.x, E = p.E;
   const int per_chunk = p.tpc * p.k;   // assignments per full chunk (<= 256)
   const int64_t M = p.T * p.k;
@@ -218,7 +230,7 @@ __device__ void leader(const RouteParams& p, int s, int* smem, int lds_ints) {
     __syncthreads();
   }
   for (int e = tid; e < E; e += kThreads) store_coherent(&p.super[(int64_t)s * E + e], run[e]);
-  publish(&p.flags[s], p.tag);
+  publish(&p.flags[s], tag);
 }
 
 // MX quant of one half of a 32-element block (16 bf16 in u0, u1); the other
@@ -252,19 +264,23 @@ __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteParams p) {
   // tables] [kThreads ints: s_pos] [the share's quantised rows, row_bytes each]
   extern __shared__ __align__(16) int dyn[];
   __shared__ int s_wsum[kThreads / 64];
+  __shared__ uint64_t s_gen;   // the workspace's generation word, read once by thread 0
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.E;
   if (!kSingle && (int)blockIdx.x < p.S) {   // uniform per block
-    leader(p, blockIdx.x, dyn, p.lds_ints);
+    if (tid == 0) s_gen = __hip_atomic_load(p.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint64_t tag = call_tag(p, s_gen);
+    leader(p, blockIdx.x, dyn, p.lds_ints, tag);
     if (blockIdx.x == 0) {
       // gather the leaders' flags into the one flag the scatter workgroups
       // poll (left unset if a leader has not finished in time: the scatter
       // workgroups then count for themselves)
       bool ok = true;
-      if (tid < p.S) ok = wait_flag(&p.flags[tid], p.tag, p.wait_limit);
+      if (tid < p.S) ok = wait_flag(&p.flags[tid], tag, p.wait_limit);
       if (__syncthreads_and(ok) && tid == 0)
-        __hip_atomic_store(&p.flags[p.S], p.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.flags[p.S], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
@@ -287,7 +303,13 @@ __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteParams p) {
   // (thread 0 also looks at the ready flag, in the same memory round trip as
   // the ids)
   bool seen = true;
-  if (!single && tid == 0) seen = load_flag(&p.flags[p.S]) == p.tag;
+  uint64_t tag = 0;
+  if (!single && tid == 0) {
+    const uint64_t g = __hip_atomic_load(p.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t f = load_flag(&p.flags[p.S]);
+    tag = call_tag(p, g);
+    seen = f == tag;
+  }
   const int64_t a0 = (int64_t)c * p.tpc * p.k;
   const int na = (int)std::min<int64_t>((int64_t)p.tpc * p.k, M - a0);
   const int64_t a = a0 + tid;
@@ -381,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteParams p) {
       // thread 0 polls the ready flag; the barrier orders every wave's count
       // loads after it was seen
       bool ok = true;
-      if (tid == 0) ok = wait_flag(&p.flags[p.S], p.tag, p.wait_limit);
+      if (tid == 0) ok = wait_flag(&p.flags[p.S], tag, p.wait_limit);   // thread 0 holds the tag
       ready = __syncthreads_and(ok) ? 1 : 0;
     } else {
       __syncthreads();   // the per-wave counts are read: their LDS is reused below
@@ -490,6 +512,12 @@ __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteParams p) {
   }
 }
 
+// Advances a routing workspace's generation word (recorded before the
+// routing kernel when the stream is capturing).
+__global__ void bump_generation(uint64_t* gen) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *gen += 1;
+}
+
 __global__ void zero_i64(int64_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -541,7 +569,7 @@ std::atomic<int64_t> g_wait_limit{(int64_t)1 << 18};
 size_t route_workspace_bytes(int64_t T, int64_t k, int64_t E) {
   const Split s = split_of(T, k);
   if (s.S == 0) return 0;
-  return align_up((size_t)(E * s.nch) * 4, 256) + align_up((size_t)(E * s.S) * 4, 256) +
+  return kCtrlBytes + align_up((size_t)(E * s.nch) * 4, 256) + align_up((size_t)(E * s.S) * 4, 256) +
          align_up((size_t)(s.S + 1) * 8, 256);
 }
 
@@ -579,6 +607,8 @@ int launch_route_quant(const uint16_t* x, const int32_t* ids, int64_t T, int64_t
   p.group_list = group_list;
   if (sp.S > 0) {
     char* w = static_cast<char*>(ws);
+    p.gen = reinterpret_cast<const uint64_t*>(w);
+    w += kCtrlBytes;
     const size_t pre_bytes = align_up((size_t)(E * sp.nch) * 4, 256);
     p.chunk_pre = reinterpret_cast<int32_t*>(w);
     p.super = reinterpret_cast<int32_t*>(w + pre_bytes);
@@ -617,10 +647,19 @@ int launch_route_quant(const uint16_t* x, const int32_t* ids, int64_t T, int64_t
   p.lds_ints = (int)(lds / 4);
   p.scales16 = (reinterpret_cast<uintptr_t>(xs) % 16 == 0 && s_stride % 16 == 0) ? 1 : 0;
   const int64_t grid = sp.S + sp.nch * split;
-  if (sp.S == 0)
+  if (sp.S == 0) {
     route_quant_kernel<true><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(p);
-  else
+  } else {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess)
+      return fail(MX_ERR_HIP, "moe_route_quant: hipStreamIsCapturing failed");
+    if (cs == hipStreamCaptureStatusActive) {
+      bump_generation<<<dim3(1), dim3(64), 0, stream>>>(static_cast<uint64_t*>(ws));
+      const int rc = check_launch("moe_route_quant(generation)");
+      if (rc) return rc;
+    }
     route_quant_kernel<false><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(p);
+  }
   return check_launch("route_quant_kernel");
 }
 

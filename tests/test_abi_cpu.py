@@ -89,11 +89,11 @@ def test_route_noalloc_validation(lib):
     assert f(None, FAKE, 64, 256, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
     assert f(FAKE, FAKE, 64, 256, 2, 8, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
     # E = 1024, top-8: 4 KB of counts per 32-token routing chunk, plus the
-    # super-chunk offsets (128 KB) and flags: 991 chunks fit in 4 MiB
+    # control block, the super-chunk totals (128 KB) and flags: 991 chunks fit in 4 MiB
     assert mx.route_workspace_size(31712, 8, 1024) <= 4 << 20 < mx.route_workspace_size(31713, 8, 1024)
     assert args(31713, 256, 8, 1024) == UNSUPPORTED
     assert "routing scratch" in mx.last_error()
-    assert mx.route_workspace_size(261088, 8, 128) <= 4 << 20 < mx.route_workspace_size(261089, 8, 128)
+    assert mx.route_workspace_size(261056, 8, 128) <= 4 << 20 < mx.route_workspace_size(261057, 8, 128)
 
 
 def test_pack_validation(lib):

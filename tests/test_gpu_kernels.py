@@ -208,6 +208,65 @@ def test_route_quant_reused_workspace():
         assert np.array_equal(host(xs), rs)
 
 
+def route_graph_replays(call, T=2049, K=256, k=8, E=64, seed=5):
+    """Captures `call(x, ids, outs)` (one routing call on the current stream)
+    in a HIP graph, then replays it on three new inputs copied into the
+    captured buffers, with eager routing calls and synchronisations between
+    the replays; every replay and every eager call is checked against the
+    oracle.  The inputs change between replays, so a replay that accepted an
+    earlier replay's published counts would place rows wrongly."""
+    rng = np.random.default_rng(seed)
+    M = T * k
+    sets = []
+    for i in range(4):
+        x = to_bf16_bits((rng.standard_normal((T, K)) * np.exp2(rng.integers(-6, 6, (T, 1)))).astype(np.float32))
+        ids = np.stack([rng.choice(E, size=k, replace=False,
+                                   p=None if i % 2 == 0 else np.r_[[0.3], np.full(E - 1, 0.7 / (E - 1))])
+                        for _ in range(T)]).astype(np.int32)
+        sets.append((x, ids))
+    x_buf, ids_buf = bf16_dev(sets[0][0]), i32_dev(sets[0][1])
+
+    def new_outs():
+        return (torch.empty((M, K), dtype=torch.uint8, device="cuda"),
+                torch.empty((M, K // 64, 2), dtype=torch.uint8, device="cuda"),
+                torch.empty(M, dtype=torch.int32, device="cuda"), torch.empty(M, dtype=torch.int32, device="cuda"),
+                torch.empty(E, dtype=torch.int64, device="cuda"))
+
+    def check(outs, x, ids, what):
+        ref = moe_ref.route_quant_ref(x, ids, E)
+        for name, g, r in zip(("xq", "xs", "sorted_row", "expanded_row_idx", "group_list"), outs, ref):
+            assert np.array_equal(host(g), r), (what, name)
+
+    outs = new_outs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture
+        call(x_buf, ids_buf, outs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    check(outs, *sets[0], "warm-up")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(x_buf, ids_buf, outs)
+    for i in (1, 2, 3):
+        x_buf.copy_(bf16_dev(sets[i][0]))
+        ids_buf.copy_(i32_dev(sets[i][1]))
+        say(f"graph replay {i}")
+        graph.replay()
+        torch.cuda.synchronize()
+        check(outs, *sets[i], f"replay {i}")
+        eager = new_outs()
+        call(bf16_dev(sets[i - 1][0]), i32_dev(sets[i - 1][1]), eager)
+        torch.cuda.synchronize()
+        check(eager, *sets[i - 1], f"eager call after replay {i}")
+
+
+def test_route_quant_graph_replays():
+    T, k, E = 2049, 8, 64
+    ws = torch.empty(mx.route_workspace_size(T, k, E), dtype=torch.uint8, device="cuda")
+    route_graph_replays(lambda x, ids, outs: mx.moe_route_quant(x, ids, E, out=outs, workspace=ws), T=T, k=k, E=E)
+
+
 def test_route_quant_empty_batch():
     say("moe_route_quant T=0")
     x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")

@@ -65,3 +65,11 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
     torch.cuda.synchronize()
     for r, g in zip(ref, got):
         assert np.array_equal(host(r), host(g))
+
+
+def test_noalloc_graph_replays():
+    """Captured in a HIP graph (the callers this entry point is for), replayed
+    on new inputs: every replay routes its own inputs."""
+    from test_gpu_kernels import route_graph_replays
+    E = 64
+    route_graph_replays(lambda x, ids, outs: mx.moe_route_quant_noalloc(x, ids, E, out=outs), E=E, seed=11)
