@@ -187,3 +187,40 @@ def test_explicit_stream_argument():
     for o in outs + [o2]:
         assert np.array_equal(bf16_host(o), ref)
     assert np.array_equal(host(xq), inter["xq"]) and np.array_equal(host(hq), inter["hq"])
+
+
+def test_forward_graph_replays():
+    """The whole layer captured in a HIP graph and replayed on three new
+    inputs (new tokens, routing and weights copied into the captured
+    buffers), with eager forwards and synchronisations between replays:
+    every replay equals the eager forward on the same inputs, bit for bit."""
+    cfg = custom_config("graph", 513, 512, 256, 16, 8)
+    T, K, I, E, k = cfg.T, cfg.K, cfg.I, cfg.E, cfg.k
+    sets = [make_inputs(custom_config(f"graph{i}", T, K, I, E, k), seed=20 + i) for i in range(4)]
+    wdev = _device_weights(sets[0])
+    x, ids, w = bf16_dev(sets[0]["x"]), i32_dev(sets[0]["topk_ids"]), f32_dev(sets[0]["topk_w"])
+    ws = mx.forward_workspace(T, K, I, E, k)
+    out = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture
+        mx.moe_mxfp8_forward(x, ids, w, *wdev, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mx.moe_mxfp8_forward(x, ids, w, *wdev, out=out, workspace=ws)
+    for i in (1, 2, 3):
+        d = sets[i]
+        x.copy_(bf16_dev(d["x"]))
+        ids.copy_(i32_dev(d["topk_ids"]))
+        w.copy_(f32_dev(d["topk_w"]))
+        say(f"moe_mxfp8_forward graph replay {i}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = bf16_host(out)
+        eager_ws = mx.forward_workspace(T, K, I, E, k)
+        eager = mx.moe_mxfp8_forward(bf16_dev(d["x"]), i32_dev(d["topk_ids"]), f32_dev(d["topk_w"]), *wdev,
+                                     workspace=eager_ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, bf16_host(eager)), i
