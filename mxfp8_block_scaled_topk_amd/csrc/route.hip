@@ -698,12 +698,12 @@ extern "C" int moe_route_quant(const void* x_bf16, const int32_t* topk_ids, int6
 // ---------------------------------------------------------------------------
 // moe_route_quant_noalloc: the same routing for callers that cannot allocate
 // (code under graph capture, tight serving loops).  The only scratch the
-// routing kernels use -- per-chunk expert counts, scanned in place, and the
-// experts' totals -- lives in this file-scope device array instead of a
-// caller workspace.  Every element the kernels read is first written by the
-// same call (the histogram writes every chunk's count of every expert, the
-// scan every total), so nothing needs clearing between calls; calls that
-// overlap on one GPU share the array and race.
+// routing kernel uses -- the generation word, per-chunk expert counts, the
+// super-chunk totals and the flags that publish them -- lives in this
+// file-scope device array instead of a caller workspace.  Every count the
+// kernel reads is first written by the same call, and a flag matches only the
+// tag of the call (or graph replay) that set it, so nothing needs clearing
+// between calls; calls that overlap on one GPU share the array and race.
 // ---------------------------------------------------------------------------
 
 namespace mxmoe {
