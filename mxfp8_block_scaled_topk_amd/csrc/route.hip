@@ -137,7 +137,7 @@ __device__ bool wait_flag(const uint64_t* f, uint64_t tag, int64_t limit) {
 }
 
 // Cross-workgroup exchange.  Everything one workgroup publishes to another
-// (counts, offsets, flags) is written and read with device-scope accesses
+// (counts and flags) is written and read with device-scope accesses
 // (agent-scope atomics: loads and stores carrying the device scope bits), which
 // go to the device's coherence point instead of a compute unit's or an XCD's
 // own cache.  A publisher waits until its device-scope stores are complete
@@ -260,8 +260,9 @@ __device__ __forceinline__ void quant_half_block(const RouteParams& p, int64_t t
 // kSingle: all assignments in one chunk (no leaders, no waits).
 template <bool kSingle>
 __global__ __launch_bounds__(kThreads) void route_quant_kernel(RouteParams p) {
-  // dynamic LDS: [4E ints: per-wave expert counts; the leader's and block 0's
-  // tables] [kThreads ints: s_pos] [the share's quantised rows, row_bytes each]
+  // dynamic LDS: [4E ints: per-wave expert counts, or a leader's chunk counts
+  // (its whole LDS)] [kThreads ints: s_pos] [the share's quantised rows,
+  // row_bytes each]
   extern __shared__ __align__(16) int dyn[];
   __shared__ int s_wsum[kThreads / 64];
   __shared__ uint64_t s_gen;   // the workspace's generation word, read once by thread 0
