@@ -318,8 +318,9 @@ def _mx_operands(M, Kd, E, N, spread=4):
 
 # The library picks 128-token tiles (three-slot ring) when Kd >= 384 and the
 # experts average at most 64 rows (M <= 64 E), else 256-token tiles: here
-# the *-128, *-3stage, *-4stage and decode-* cases (empty experts appended
-# where needed) take the 128-row kernel, the rest the 256-row one.
+# the *-128, *-3stage, *-4stage, decode-*, few-rows-* and many-tiles cases
+# (empty experts appended where needed) take the 128-row kernel, the rest the
+# 256-row one.
 GMM_CASES = {
     "ragged": ([0, 1, 127, 128, 129, 255, 256, 257, 300, 0, 5], 256, 256),
     "single-expert": ([515], 384, 256),
@@ -343,6 +344,13 @@ GMM_CASES = {
     # 128-row tiles with 4 k stages: tails at 16/32/128 rows; 1024 tiles
     "small-tiles-4stage": ([16, 17, 31, 32, 33, 127, 128, 129, 0, 255, 1] + [0] * 2, 512, 512),
     "decode-many-tiles-4stage": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 512, 1024),
+    # 128-row tiles, 512 of them (two per CU): the ring carries across tiles
+    "few-rows-many-tiles": ([6, 7, 5, 9, 6, 8, 10, 5] * 16, 384, 1024),
+    "few-rows-many-tiles-4stage": ([6, 7, 5, 9, 6, 8, 10, 5] * 16, 512, 1024),
+    # mostly empty experts beside a few of 32-70 rows (256-row tiles, K = 256)
+    "sparse-ragged": ([70, 33, 32, 1, 2] + [0] * 40, 256, 256),
+    # 128-row tiles, 1024 of them (four per CU), 3 k stages
+    "many-tiles": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 384, 2048),
 }
 
 
@@ -421,7 +429,8 @@ def test_gmm_mx_guard_bands_and_untouched_rows():
     assert np.all(yh[199:] == 0x5A5A)                  # rows past the last expert untouched
 
 
-# (128-row tiles: single, tail-boundaries-128, *-3stage, *-4stage, decode-*)
+# (128-row tiles: single, tail-boundaries-128, *-3stage, *-4stage, decode-*,
+# few-rows-*, many-tiles)
 GMM1_CASES = {
     "ragged": ([3, 0, 128, 129, 1, 260, 256, 511], 256, 128),
     "wide-i": ([70, 150], 128, 384),
@@ -435,6 +444,11 @@ GMM1_CASES = {
     "decode-many-tiles": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 384, 512),
     "small-tiles-4stage": ([16, 17, 31, 32, 33, 127, 128, 129, 0, 255, 1] + [0] * 2, 512, 256),
     "decode-many-tiles-4stage": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 512, 512),
+    "few-rows-many-tiles": ([6, 7, 5, 9, 6, 8, 10, 5] * 16, 384, 512),
+    "few-rows-many-tiles-4stage": ([6, 7, 5, 9, 6, 8, 10, 5] * 16, 512, 512),
+    "sparse-ragged": ([70, 33, 32, 1, 2] + [0] * 40, 256, 128),
+    # 1024 tiles (four per CU), 4 k stages
+    "many-tiles": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 512, 1024),
 }
 
 
@@ -477,13 +491,14 @@ def _checkpoint_bytes(rng, shape):
 
 
 @pytest.mark.parametrize("kd", [256, 384, 512])
-def test_gmm_max_experts(kd):
+@pytest.mark.parametrize("rows", [(0, 4), (4, 13)])
+def test_gmm_max_experts(kd, rows):
     """Both GEMMs at the largest expert count the kernels take (1024), with
-    0-3 rows per expert: Kd = 256 runs the 256-row tiles, Kd = 384 and 512
-    the 128-row tiles with the three-slot ring (3 and 4 k stages)."""
-    rng = np.random.default_rng(1024 + kd)
+    0-3 and 4-12 rows per expert: Kd = 256 runs the 256-row tiles, Kd = 384
+    and 512 the 128-row tiles with the three-slot ring (3 and 4 k stages)."""
+    rng = np.random.default_rng(1024 + kd + rows[0])
     E, N, I = 1024, 256, 128
-    counts = rng.integers(0, 4, E).astype(np.int64)
+    counts = rng.integers(rows[0], rows[1], E).astype(np.int64)
     M = int(counts.sum())
     say(f"gmm_mx / gmm_swiglu_mxquant E={E} M={M} Kd={kd}")
     aq, as_ = mx_ref.mx_quantize_ref(rng.standard_normal((M, kd)))

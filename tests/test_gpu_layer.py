@@ -66,6 +66,9 @@ def _check_routing_and_xq(d, inter):
     ("several-tiles", (300, 512, 256, 12, 4)),
     ("sparse-experts", (129, 256, 128, 70, 3)),
     ("k1-ragged", (333, 256, 128, 3, 1)),
+    # decode-sized: one row per expert on average (GEMM1 on 128-row tiles)
+    ("decode-small", (16, 512, 256, 64, 4)),
+    ("decode-i384", (8, 768, 384, 32, 8)),
 ])
 def test_forward_small_full_compare(shape):
     name, dims = shape
