@@ -80,25 +80,31 @@ __device__ __forceinline__ float quad_swapf1(float x) {
 __device__ __forceinline__ float quad_swapf2(float x) {
   return __int_as_float(quad_swap<kQuadXor2>(__float_as_int(x)));
 }
-// Exchange with the lane whose index differs in bit 2 (ds_swizzle, xor mask 4
-// within each 32-lane half).
-__device__ __forceinline__ int swap4(int x) { return __builtin_amdgcn_ds_swizzle(x, 0x101f); }
-__device__ __forceinline__ float swapf4(float x) { return __int_as_float(swap4(__float_as_int(x))); }
-// Reductions over the 8 lanes (an aligned group) that hold one token.
+// The other quad of the lane's aligned group of 8 (DPP row_half_mirror: lane
+// i of each 8 takes lane 7 - i).  Applied to a value that is uniform within
+// each quad, it swaps the group's two quads, with no trip through the LDS
+// unit as a ds_swizzle exchange would take.
+constexpr int kHalfMirror = 0x141;
+__device__ __forceinline__ int other_quad(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, kHalfMirror, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float other_quadf(float x) { return __int_as_float(other_quad(__float_as_int(x))); }
+// Reductions over the 8 lanes (an aligned group) that hold one token: within
+// each quad, then across the group's two quads.
 __device__ __forceinline__ float oct_max(float x) {
   x = fmaxf(x, quad_swapf1(x));
   x = fmaxf(x, quad_swapf2(x));
-  return fmaxf(x, swapf4(x));
+  return fmaxf(x, other_quadf(x));
 }
 __device__ __forceinline__ float oct_sum(float x) {
   x += quad_swapf1(x);
   x += quad_swapf2(x);
-  return x + swapf4(x);
+  return x + other_quadf(x);
 }
 __device__ __forceinline__ int oct_min(int x) {
   x = min(x, quad_swap<kQuadXor1>(x));
   x = min(x, quad_swap<kQuadXor2>(x));
-  return min(x, swap4(x));
+  return min(x, other_quad(x));
 }
 template <int NT>   // gate rows held per chunk: 64 NT (E <= 64 NT)
 __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __restrict__ x,
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
   // ---- per token: softmax, top-k, weights --------------------------------------
   // 8 lanes per token (the 512 threads cover the 64 tokens): lane q holds the
   // logits of experts 8 i + q in registers; reductions across the 8 use DPP
-  // quad permutes and one swizzle.  A taken (or absent) expert is NaN.
+  // permutes only.  A taken (or absent) expert is NaN.
   {
     constexpr int NPER = 8 * NT;           // experts per lane (E <= 64 NT)
     const int t = tid >> 3, q = tid & 7;
@@ -240,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
     float ls4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < NPER; ++i)
-      if (v[i] == v[i]) ls4[i & 3] += expf(v[i] - m);
+      if (v[i] == v[i]) ls4[i & 3] += __expf(v[i] - m);
     const float sum = oct_sum((ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
     const int64_t o = (t0 + t) * k;
     float wsel = 0.0f;
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const uint16_t* __rest
 #pragma unroll
       for (int i = 0; i < NPER; ++i)
         if (8 * i + q == be) v[i] = NAN;
-      const float pe = expf(bv - m);
+      const float pe = __expf(bv - m);
       wsel += pe;
       if (q == 0) lt[j] = pe;             // the row's logits are in registers now
       if (q == 0 && live) topk_ids[o + j] = be;
