@@ -107,14 +107,20 @@ struct GmmParams {
 
 constexpr int SK = 128;          // K bytes per stage (whole 128-byte rows)
 
-// One ring slot: a k stage of both operands and their scale words, for a
-// tile of kRows token rows.
-template <int kRows>
+// One ring slot: a k stage of both operands for a tile of kRows token rows,
+// and with per-stage scale loads (kScales) the stage's scale word of every
+// row (4 bytes: its four 32-blocks).
+template <int kRows, bool kScales>
 struct StageT {
   uint8_t a[BN * SK];
   uint8_t b[kRows * SK];
   uint32_t sa[BN];
   uint32_t sb[kRows];
+};
+template <int kRows>
+struct StageT<kRows, false> {
+  uint8_t a[BN * SK];
+  uint8_t b[kRows * SK];
 };
 
 // Group-list types: 0 cumulative, 1 counts (the entry points' two forms);
@@ -219,14 +225,17 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 // kBM: token rows per tile.  256: the two-slot ring above.  128 (few rows
 // per expert, e.g. decode batches, where the weight stream is latency-bound
 // rather than MFMA-bound): each wave holds one 32-token fragment, a slot is
-// 49.5 KB, and three slots give the DMA two stages of lead; per-stage scale
-// loads only (the scale ring would not fit) and at least 3 k stages.
+// 48 KB (49.5 KB with per-stage scale words), and three slots give the DMA
+// two stages of lead; at least 3 k stages.  The scale ring then holds 256
+// weight rows and 128 token rows per group (12 KB for both buffers), which
+// fits beside the three slots while the per-expert tables, sized to E in the
+// dynamic LDS, take at most 4 KB (E <= 511, host).
 template <bool kSwiglu, int kWF, int kG, int kBM>
 __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   constexpr bool kW4 = kWF == kWfE2m1;
   constexpr bool kPk = kWF == kWfPacked;
   static_assert(kG == 1 || kG == 4, "scale groups of 1 or 4 stages");
-  static_assert(kBM == 256 || (kBM == 128 && kG == 1), "128-row tiles use per-stage scale loads");
+  static_assert(kBM == 256 || kBM == 128, "256- or 128-row tiles");
   constexpr int kSl = kBM == 256 ? 2 : 3;   // LDS ring slots
   constexpr int kNB = kBM / 128;            // 32-token B fragments per wave
   constexpr int kTokRows = kBM / 8;         // token rows each wave's DMA fetches
@@ -234,13 +243,16 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   constexpr int kNA = kW4 ? 2 : 4;          // weight DMAs per wave per stage
   constexpr int kDmaOps = kNA + kNT + 1;    // + 1 scale load
   constexpr int kRowA = kW4 ? SK / 2 : SK;  // weight bytes per LDS row per stage
-  using Stage = StageT<kBM>;
+  using Stage = StageT<kBM, kG == 1>;
   __shared__ __attribute__((aligned(16))) Stage st[kSl];
-  __shared__ int s_tile0[kMaxE + 1];
-  __shared__ int s_row0[kMaxE + 1];
   // kG = 4: scale words of 4 consecutive stages; group buffer (g/4)%2 holds
-  // 256 weight rows then 256 token rows, 16 bytes per row
-  __shared__ __attribute__((aligned(16))) uint32_t s_sc[kG == 4 ? 2 * 2 * 256 * 4 : 4];
+  // 256 weight rows then kBM token rows, 16 bytes per row
+  constexpr uint32_t kScBuf = (BN + kBM) * 16;   // bytes per group buffer
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[kG == 4 ? 2 * kScBuf / 4 : 4];
+  // per-expert tables (E + 1 ints each) in the dynamic LDS, sized by the launch
+  extern __shared__ int s_tab[];
+  int* const s_tile0 = s_tab;
+  int* const s_row0 = s_tab + (p.E + 1);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -415,8 +427,10 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   // token scales (rows past M repeat the last row).  Offsets are byte
   // offsets clamped with one min against a scalar cap, so the DMA path has
   // no multiply and no branch.
-  const uint32_t s_lds = wave < 4 ? (uint32_t)offsetof(Stage, sa) + (uint32_t)(256 * wave)
-                                  : (uint32_t)offsetof(Stage, sb) + (uint32_t)(256 * (wave - 4));
+  uint32_t s_lds = 0;   // kG = 1: the wave's 64 scale words in the slot
+  if constexpr (kG == 1)
+    s_lds = wave < 4 ? (uint32_t)offsetof(Stage, sa) + (uint32_t)(256 * wave)
+                     : (uint32_t)offsetof(Stage, sb) + (uint32_t)(256 * (wave - 4));
   const uint32_t s_lane = wave < 4 ? lane_s : (uint32_t)((64 * (wave - 4) + lane) * srow);
   auto s_voff = [&](int last) __attribute__((always_inline)) -> uint32_t {
     const uint32_t cap = wave < 4 ? 0xffffffffu : (uint32_t)(last * srow);
@@ -446,12 +460,14 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     if constexpr (kSl == 2) return gs & 1;
     else return (int)((unsigned)gs % 3u);
   };
-  // VMEM instructions this wave issues for one stage's DMA (kSl = 3: the
-  // mid-stage wait leaves the latest stage in flight; loads retire in order)
-  auto dma_count = [&](const Src& src) __attribute__((always_inline)) -> int {
-    return kNA + (src.tok ? kNT : 0) + (sc_dma ? 1 : 0);
+  // VMEM instructions this wave issues for the DMA of tile stage ks (kSl =
+  // 3: the mid-stage wait leaves the latest stage in flight; loads retire in
+  // order, so the count must be exact); with kG = 4 only a group's first
+  // stage carries the scale load
+  auto dma_count = [&](const Src& src, int ks) __attribute__((always_inline)) -> int {
+    return kNA + (src.tok ? kNT : 0) + ((sc_dma && (kG == 1 || (ks & 3) == 0)) ? 1 : 0);
   };
-  const uint32_t s_lds4 = wave < 4 ? (uint32_t)(1024 * wave) : (uint32_t)(4096 + 1024 * (wave - 4));
+  const uint32_t s_lds4 = wave < 4 ? (uint32_t)(1024 * wave) : (uint32_t)(BN * 16 + 1024 * (wave - 4));
   // One DMA instruction of k stage ks of the tile whose source is `src`,
   // global stage gs (ring slot gs%2): i = 0..3 weight rows, 4..7 token rows,
   // 8 scales.
@@ -484,10 +500,12 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
         dma16(voff, src.arow, base + (uint32_t)offsetof(Stage, b) + (uint32_t)((kTokRows * wave + 8 * j) * SK));
     } else if constexpr (kG == 1) {
       if (sc_dma) dma4(s_voff(src.last) + (uint32_t)(kr * 4), src.srowp, base + s_lds);
-    } else if ((ks & 3) == 0) {
-      // the group's 16 bytes per row, from its first stage in memory
+    } else if (sc_dma && (ks & 3) == 0) {
+      // the group's 16 bytes per row, from its first stage in memory (with
+      // 128-row tiles waves 6 and 7 have no scale rows: their ring offsets
+      // would lie past the 6 KB group buffer)
       dma16(s_voff(src.last) + (uint32_t)((kr & ~3) * 4), src.srowp,
-            sc_base + (uint32_t)(((gs >> 2) & 1) * 8192) + s_lds4);
+            sc_base + (uint32_t)(((gs >> 2) & 1) * kScBuf) + s_lds4);
     }
   };
   auto dma_stage = [&](const Src& src, int ks, int gs) __attribute__((always_inline)) {
@@ -500,10 +518,13 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   const int sw = (li >> 1) & 7;
   const uint32_t rd_a = (uint32_t)offsetof(Stage, a) + (uint32_t)((128 * wn + li) * kRowA);
   const uint32_t rd_b = (uint32_t)offsetof(Stage, b) + (uint32_t)((32 * kNB * wm + li) * SK);
-  const uint32_t rd_sa = (uint32_t)offsetof(Stage, sa) + (uint32_t)((128 * wn + li) * 4);
-  const uint32_t rd_sb = (uint32_t)offsetof(Stage, sb) + (uint32_t)((32 * kNB * wm + li) * 4);
+  uint32_t rd_sa = 0, rd_sb = 0;   // kG = 1: scale words in the slot
+  if constexpr (kG == 1) {
+    rd_sa = (uint32_t)offsetof(Stage, sa) + (uint32_t)((128 * wn + li) * 4);
+    rd_sb = (uint32_t)offsetof(Stage, sb) + (uint32_t)((32 * kNB * wm + li) * 4);
+  }
   const uint32_t rd_sa4 = (uint32_t)((128 * wn + li) * 16);          // kG = 4 scale ring
-  const uint32_t rd_sb4 = (uint32_t)(4096 + (64 * wm + li) * 16);
+  const uint32_t rd_sb4 = (uint32_t)(BN * 16 + (32 * kNB * wm + li) * 16);
   uint32_t chk[4];   // byte offset of logical chunk 2c + lg within a row
 #pragma unroll
   for (int c = 0; c < 4; ++c) chk[c] = (uint32_t)(((2 * c + lg) ^ sw) << 4);
@@ -527,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
   // tiles start at multiples of 4) sit at word (ks + rot) % 4 of each row's
   // 16 bytes in group buffer (gs/4)%2
   auto group_ptr = [&](int gs) __attribute__((always_inline)) {
-    uint32_t b = sc_base + (uint32_t)(((gs >> 2) & 1) * 8192 + (((gs & 3) + cur_r) & 3) * 4);
+    uint32_t b = sc_base + (uint32_t)(((gs >> 2) & 1) * kScBuf + (((gs & 3) + cur_r) & 3) * 4);
     asm("" : "+s"(b));
     return (const lds_u8*)(uintptr_t)b;
   };
@@ -688,7 +709,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
             for (int i = 5; i < kDmaOps; ++i) dma_part(i, t, tks, g + kSl);
           }
         });
-        if constexpr (kSl == 3) last_cnt = dma_count(t);
+        if constexpr (kSl == 3) last_cnt = dma_count(t, tks);
       } else {
         substep(g + 1, 0, std::false_type{}, [&](int) {});   // the next tile reloads at its start
       }
@@ -708,9 +729,9 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
       // 16-byte chunk c at physical chunk c ^ (r%16), and its two 8-byte
       // halves swapped when r >= 16, so both the writes (lane = token) and
       // the reads (16 lanes per row) are free of bank conflicts.  With
-      // 128-row tiles the 8 KB per wave do not fit one 49.5 KB slot for all
-      // 8 waves: waves 0-3 go first, then (after a barrier) waves 4-7 reuse
-      // the same regions.
+      // 128-row tiles the 8 KB per wave do not fit one 48 KB slot for all 8
+      // waves: waves 0-3 go first, then (after a barrier) waves 4-7 reuse the
+      // same regions.
       const int64_t N = p.Nw;
       constexpr int kRounds = kBM == 256 ? 1 : 2;
 #pragma unroll
@@ -829,7 +850,7 @@ __global__ __launch_bounds__(kThreads) void gmm_kernel(GmmParams p) {
     if constexpr (kSl == 3) {
       if (has_next) {
         dma_stage(nsrc, 2, g + 2);
-        last_cnt = dma_count(nsrc);
+        last_cnt = dma_count(nsrc, 2);
       }
     } else if (nk > 1) {
       if (has_next) dma_stage(nsrc, 1, g + 1);
@@ -858,18 +879,38 @@ int launch(const GmmParams& p, hipStream_t stream, const char* name) {
   int64_t grid = (int64_t)num_cus() / 8 * 8;
   if (grid < 8) grid = 8;
   if (grid > (upper + 7) / 8 * 8) grid = (upper + 7) / 8 * 8;
-  if (small) {
-    gmm_kernel<kSwiglu, kWF, 1, 128><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
-    return check_launch(name);
-  }
+  const dim3 g3((unsigned)grid), b3(kThreads);
+  // the per-expert tables (dynamic LDS)
+  const size_t tab = (size_t)(p.E + 1) * 2 * sizeof(int);
   // scale groups of 4 stages when the k stages divide into them and both
-  // scale tensors are 16-byte aligned (every scale row then is)
+  // scale tensors are 16-byte aligned (every scale row then is); with
+  // 128-row tiles also only while the scale ring fits beside the three slots
   const bool groups = (p.Kd / BK) % 4 == 0 && reinterpret_cast<uintptr_t>(p.as) % 16 == 0 &&
                       reinterpret_cast<uintptr_t>(p.ws) % 16 == 0;
+  if (small) {
+    // LDS left for the tables beside that kernel's static LDS (as compiled),
+    // read once; 0 if the query fails (then per-stage scale loads)
+    static const size_t room = [] {
+      hipFuncAttributes a{};
+      int dev = 0, lim = 0;
+      if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(gmm_kernel<kSwiglu, kWF, 4, 128>)) != hipSuccess ||
+          hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return (size_t)0;
+      }
+      return a.sharedSizeBytes < (size_t)lim ? (size_t)lim - a.sharedSizeBytes : (size_t)0;
+    }();
+    if (groups && tab <= room)
+      gmm_kernel<kSwiglu, kWF, 4, 128><<<g3, b3, tab, stream>>>(p);
+    else
+      gmm_kernel<kSwiglu, kWF, 1, 128><<<g3, b3, tab, stream>>>(p);
+    return check_launch(name);
+  }
   if (groups)
-    gmm_kernel<kSwiglu, kWF, 4, 256><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    gmm_kernel<kSwiglu, kWF, 4, 256><<<g3, b3, tab, stream>>>(p);
   else
-    gmm_kernel<kSwiglu, kWF, 1, 256><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(p);
+    gmm_kernel<kSwiglu, kWF, 1, 256><<<g3, b3, tab, stream>>>(p);
   return check_launch(name);
 }
 
