@@ -341,7 +341,11 @@ GMM_CASES = {
     "decode-like": ([2, 3, 0, 1, 2, 2, 0, 4] * 8, 768, 256),
     # 512 tiles, two per CU: the ring carries across tile boundaries
     "decode-many-tiles": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 384, 1024),
-    # 128-row tiles with 4 k stages: tails at 16/32/128 rows; 1024 tiles
+    # 128-row tiles with 4 k stages (one scale group per tile): tails at
+    # 16/32/128 rows; 1024 tiles.  decode-many-tiles-4stage runs two tiles per
+    # CU, so the second tile reads the expert tables after the scale ring's
+    # second buffer has been written (waves 6 and 7, which have no scale
+    # rows, must not write past that buffer)
     "small-tiles-4stage": ([16, 17, 31, 32, 33, 127, 128, 129, 0, 255, 1] + [0] * 2, 512, 512),
     "decode-many-tiles-4stage": ([2, 3, 1, 1, 2, 2, 5, 4] * 16, 512, 1024),
     # 128-row tiles, 512 of them (two per CU): the ring carries across tiles
