@@ -1,0 +1,101 @@
+"""Seeded random sweep of both grouped GEMMs against the oracle.
+
+Complements the hand-picked cases in test_gpu_kernels.py with drawn ones:
+expert counts from three mixes (decode-like 0-5 rows per expert, counts at and
+around the 32/64/128/256-row boundaries, and large ragged experts), reduction
+sizes that switch between per-stage scale loads (stages not a multiple of 4)
+and 4-stage scale groups, and group lists that select either tile height
+(128-token tiles when the experts average at most 64 rows and there are at
+least 3 k stages).  Each case's operands and sizes come from its own seed.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_topk_amd as mx
+from gpu_util import bf16_host, bf16_rows_rel_err, explain_hq_mismatches, host, i64_dev, row_rel_err, say, u8_dev
+from oracle import moe_ref, mx_ref
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+MAX_ROWS = 4096
+SEEDS = list(range(8))
+
+
+def draw_case(seed, n_choices):
+    """(rng, counts [E] int64, Kd, n): the case's group counts, reduction
+    size and output size (N for GEMM2, I for GEMM1) from its seed."""
+    rng = np.random.default_rng(1000 + seed)
+    kind = seed % 3
+    if kind == 0:
+        E = int(rng.choice([8, 40, 96]))
+        counts = rng.integers(0, 6, E)
+    elif kind == 1:
+        E = int(rng.choice([3, 8, 17]))
+        counts = rng.choice([0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257], E)
+    else:
+        E = int(rng.choice([1, 3, 6]))
+        counts = rng.integers(0, 700, E)
+    counts = counts.astype(np.int64)
+    while counts.sum() > MAX_ROWS:
+        counts = counts // 2
+    Kd = int(rng.choice([128, 256, 384, 512, 640, 768, 1024]))
+    n = int(rng.choice(n_choices))
+    return rng, counts, Kd, n
+
+
+def mx_operands(rng, M, Kd, E, N):
+    a = rng.standard_normal((M, Kd)) * np.exp2(rng.integers(-4, 4, (M, 1)))
+    w = rng.standard_normal((E * N, Kd)) * 0.05 * np.exp2(rng.integers(-4, 4, (E * N, 1)))
+    aq, as_ = mx_ref.mx_quantize_ref(a)
+    wq, ws = mx_ref.mx_quantize_ref(w)
+    return aq, as_, wq.reshape(E, N, Kd), ws.reshape(E, N, -1, 2)
+
+
+def tile_rows(counts, Kd):
+    """The token-tile height the library picks for these counts."""
+    M, E = int(counts.sum()), len(counts)
+    return 128 if Kd // 128 >= 3 and M <= 64 * E else 256
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_gmm_mx_sweep(seed):
+    rng, counts, Kd, N = draw_case(seed, [256, 512, 768])
+    M, E = int(counts.sum()), len(counts)
+    gl_type = int(rng.integers(0, 2))
+    say(f"gmm_mx sweep seed={seed} M={M} Kd={Kd} N={N} E={E} gl_type={gl_type} "
+        f"tiles={tile_rows(counts, Kd)} stages={Kd // 128}")
+    aq, as_, wq, ws = mx_operands(rng, M, Kd, E, N)
+    gl = counts if gl_type == 1 else np.cumsum(counts)
+    y = mx.gmm_mx(u8_dev(aq), u8_dev(as_), u8_dev(wq), u8_dev(ws), i64_dev(gl), gl_type)
+    torch.cuda.synchronize()
+    ref = moe_ref.gmm_mx_ref(aq, as_, wq, ws, gl, gl_type)
+    err = bf16_rows_rel_err(bf16_host(y), ref) if M else np.zeros(1)
+    say(f"  max row rel err {err.max():.3g}")
+    assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_gmm_swiglu_mxquant_sweep(seed):
+    rng, counts, K, I = draw_case(seed, [128, 256, 384])
+    M, E = int(counts.sum()), len(counts)
+    say(f"gmm_swiglu_mxquant sweep seed={seed} M={M} K={K} I={I} E={E} "
+        f"tiles={tile_rows(counts, K)} stages={K // 128}")
+    aq, as_, wq, ws = mx_operands(rng, M, K, E, 2 * I)
+    hq, hs, h = mx.gmm_swiglu_mxquant(u8_dev(aq), u8_dev(as_), u8_dev(wq), u8_dev(ws), i64_dev(counts), 1,
+                                      h_debug=True)
+    torch.cuda.synchronize()
+    rq, rs, rh = moe_ref.gmm_swiglu_mxquant_ref(aq, as_, wq, ws, counts, 1, I)
+    hk = host(h)
+    if M:
+        herr = row_rel_err(hk, rh)
+        say(f"  h max row rel err {herr.max():.3g}")
+        assert herr.max() <= 1e-3
+    # requant bytes exact given the kernel's own h; against the oracle's h
+    # every differing byte explained by the requant rule
+    kq, ks = mx_ref.mx_quantize_ref(hk.astype(np.float64))
+    assert np.array_equal(host(hq), kq)
+    assert np.array_equal(host(hs), ks)
+    n_mis, n_bad = explain_hq_mismatches(host(hq), host(hs), rq, rh)
+    say(f"  hq/hs mismatches vs oracle {n_mis} of {rq.size}, unexplained {n_bad}")
+    assert n_bad == 0 and n_mis <= 0.01 * max(rq.size, 1)
