@@ -1,20 +1,29 @@
-"""Seeded random sweep of both grouped GEMMs against the oracle.
+"""Seeded random sweeps of the layer's kernels against the oracle.
 
-Complements the hand-picked cases in test_gpu_kernels.py with drawn ones:
-expert counts from three mixes (decode-like 0-5 rows per expert, counts at and
-around the 32/64/128/256-row boundaries, and large ragged experts), reduction
-sizes that switch between per-stage scale loads (stages not a multiple of 4)
-and 4-stage scale groups, and group lists that select either tile height
-(128-token tiles when the experts average at most 64 rows and there are at
-least 3 k stages).  Each case's operands and sizes come from its own seed.
+Complements the hand-picked cases in test_gpu_kernels.py with drawn ones,
+each case's sizes and data from its own seed:
+
+* both grouped GEMMs: expert counts from three mixes (decode-like 0-5 rows
+  per expert, counts at and around the 32/64/128/256-row boundaries, and
+  large ragged experts), reduction sizes that switch between per-stage scale
+  loads (stages not a multiple of 4) and 4-stage scale groups, and group lists
+  that select either tile height (128-token tiles when the experts average at
+  most 64 rows and there are at least 3 k stages);
+* moe_route_quant: token counts on both sides of the one-chunk boundary and
+  up to several leader batches, expert counts up to 1024, skewed and uniform
+  expert choice; bit-exact;
+* moe_finalize: row widths on both sides of the wave-per-token layout (K a
+  multiple of 512 or not), a few dropped assignments; bit-exact.
 """
 import numpy as np
 import pytest
 import torch
 
 import mxfp8_block_scaled_topk_amd as mx
-from gpu_util import bf16_host, bf16_rows_rel_err, explain_hq_mismatches, host, i64_dev, row_rel_err, say, u8_dev
+from gpu_util import (bf16_dev, bf16_host, bf16_rows_rel_err, explain_hq_mismatches, f32_dev, host, i32_dev, i64_dev,
+                      row_rel_err, say, u8_dev)
 from oracle import moe_ref, mx_ref
+from workloads import to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -99,3 +108,55 @@ def test_gmm_swiglu_mxquant_sweep(seed):
     n_mis, n_bad = explain_hq_mismatches(host(hq), host(hs), rq, rh)
     say(f"  hq/hs mismatches vs oracle {n_mis} of {rq.size}, unexplained {n_bad}")
     assert n_bad == 0 and n_mis <= 0.01 * max(rq.size, 1)
+
+
+def rand_bf16(rng, shape, spread):
+    x = rng.standard_normal(shape) * np.exp2(rng.integers(-spread, spread + 1, shape[:-1] + (1,)))
+    return to_bf16_bits(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_route_quant_sweep(seed):
+    rng = np.random.default_rng(2000 + seed)
+    E = int(rng.choice([1, 5, 64, 128, 300, 1024]))
+    k = int(rng.integers(1, min(E, 16) + 1))
+    T = int(rng.choice([1, 7, 256 // k, 256 // k + 1, 1000, 4096, 9000]))
+    K = int(rng.choice([32, 96, 256, 2048]))
+    if T * K > 4096 * 2048:
+        K = 256
+    # skewed (a few hot experts) or uniform expert choice, distinct per token
+    p = None
+    if seed % 2:
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p = rng.permutation(p / p.sum())
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    say(f"moe_route_quant sweep seed={seed} T={T} K={K} k={k} E={E} {'skewed' if p is not None else 'uniform'}")
+    x = rand_bf16(rng, (T, K), 8)
+    xq, xs, sr, eri, gl = mx.moe_route_quant(bf16_dev(x), i32_dev(ids), E)
+    torch.cuda.synchronize()
+    rq, rs, rsr, reri, rc = moe_ref.route_quant_ref(x, ids, E)
+    assert np.array_equal(host(gl), rc)
+    assert np.array_equal(host(sr), rsr)
+    assert np.array_equal(host(eri), reri)
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(xs), rs)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_finalize_sweep(seed):
+    rng = np.random.default_rng(3000 + seed)
+    T = int(rng.choice([1, 3, 64, 333, 2048]))
+    K = int(rng.choice([8, 72, 512, 1024, 2056, 4096]))
+    k = int(rng.choice([1, 2, 6, 8]))
+    M = T * k
+    say(f"moe_finalize sweep seed={seed} T={T} K={K} k={k}")
+    y = rand_bf16(rng, (M, K), 6)
+    w = rng.random((T, k)).astype(np.float32)
+    eri = rng.permutation(M).astype(np.int32)
+    drop = rng.random(M) < 0.02                    # dropped assignments (invalid ids upstream)
+    eri[drop] = -1
+    out = mx.moe_finalize(bf16_dev(y), f32_dev(w), i32_dev(eri))
+    torch.cuda.synchronize()
+    w_eff = np.where(drop.reshape(T, k), np.float32(0.0), w)
+    ref = moe_ref.finalize_ref(y, w_eff, np.where(drop, 0, eri))
+    assert np.array_equal(bf16_host(out), ref)
