@@ -8,7 +8,9 @@ each case's sizes and data from its own seed:
   large ragged experts), reduction sizes that switch between per-stage scale
   loads (stages not a multiple of 4) and 4-stage scale groups, and group lists
   that select either tile height (128-token tiles when the experts average at
-  most 64 rows and there are at least 3 k stages);
+  most 64 rows and there are at least 3 k stages); the same weights
+  tile-packed must give the same bytes, and MXFP4 (e2m1) weights are held to
+  the same bars;
 * moe_route_quant: token counts on both sides of the one-chunk boundary and
   up to several leader batches, expert counts up to 1024, skewed and uniform
   expert choice; bit-exact;
@@ -82,6 +84,11 @@ def test_gmm_mx_sweep(seed):
     err = bf16_rows_rel_err(bf16_host(y), ref) if M else np.zeros(1)
     say(f"  max row rel err {err.max():.3g}")
     assert err.max() <= TOL
+    # the same weights tile-packed: the same bytes
+    wp = mx.mx_pack_weights(u8_dev(wq), mx.PACK_GEMM2)
+    yp = mx.gmm_mx_packed(u8_dev(aq), u8_dev(as_), wp, u8_dev(ws), i64_dev(gl), gl_type)
+    torch.cuda.synchronize()
+    assert torch.equal(yp, y)
 
 
 @pytest.mark.parametrize("seed", SEEDS)
@@ -107,6 +114,50 @@ def test_gmm_swiglu_mxquant_sweep(seed):
     assert np.array_equal(host(hs), ks)
     n_mis, n_bad = explain_hq_mismatches(host(hq), host(hs), rq, rh)
     say(f"  hq/hs mismatches vs oracle {n_mis} of {rq.size}, unexplained {n_bad}")
+    assert n_bad == 0 and n_mis <= 0.01 * max(rq.size, 1)
+    # the same weights tile-packed: the same bytes
+    wp = mx.mx_pack_weights(u8_dev(wq), mx.PACK_GEMM1)
+    hqp, hsp = mx.gmm_swiglu_mxquant_packed(u8_dev(aq), u8_dev(as_), wp, u8_dev(ws), i64_dev(counts), 1)
+    torch.cuda.synchronize()
+    assert torch.equal(hqp, hq) and torch.equal(hsp, hs)
+
+
+def w4_operands(rng, M, Kd, E, N):
+    a = rng.standard_normal((M, Kd)) * np.exp2(rng.integers(-4, 4, (M, 1)))
+    w = rng.standard_normal((E * N, Kd)) * 0.05 * np.exp2(rng.integers(-4, 4, (E * N, 1)))
+    aq, as_ = mx_ref.mx_quantize_ref(a)
+    wq, ws = mx_ref.mxfp4_quantize_ref(w)
+    return aq, as_, wq.reshape(E, N, Kd // 2), ws.reshape(E, N, -1, 2)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_gmm_w4a8_sweep(seed):
+    """Both GEMMs with MXFP4 (e2m1) weights on the GEMM sweep's drawn sizes."""
+    rng, counts, Kd, N = draw_case(seed, [256, 512, 768])
+    M, E = int(counts.sum()), len(counts)
+    say(f"w4a8 GEMM sweep seed={seed} M={M} Kd={Kd} N={N} E={E} tiles={tile_rows(counts, Kd)}")
+    aq, as_, wq, ws = w4_operands(rng, M, Kd, E, N)
+    y = mx.gmm_mx_w4a8(u8_dev(aq), u8_dev(as_), u8_dev(wq), u8_dev(ws), i64_dev(counts), 1)
+    torch.cuda.synchronize()
+    ref = moe_ref.gmm_mx_ref(aq, as_, wq, ws, counts, 1, "e2m1")
+    if M:
+        err = bf16_rows_rel_err(bf16_host(y), ref)
+        say(f"  GEMM2 max row rel err {err.max():.3g}")
+        assert err.max() <= TOL
+    I = N // 2 if (N // 2) % 128 == 0 else 128
+    aq1, as1, wq1, ws1 = w4_operands(rng, M, Kd, E, 2 * I)
+    hq, hs, h = mx.gmm_swiglu_mxquant_w4a8(u8_dev(aq1), u8_dev(as1), u8_dev(wq1), u8_dev(ws1), i64_dev(counts), 1,
+                                           h_debug=True)
+    torch.cuda.synchronize()
+    rq, rs, rh = moe_ref.gmm_swiglu_mxquant_ref(aq1, as1, wq1, ws1, counts, 1, I, "e2m1")
+    hk = host(h)
+    if M:
+        herr = row_rel_err(hk, rh)
+        say(f"  GEMM1 h max row rel err {herr.max():.3g}")
+        assert herr.max() <= 1e-3
+    kq, ks = mx_ref.mx_quantize_ref(hk.astype(np.float64))
+    assert np.array_equal(host(hq), kq) and np.array_equal(host(hs), ks)
+    n_mis, n_bad = explain_hq_mismatches(host(hq), host(hs), rq, rh)
     assert n_bad == 0 and n_mis <= 0.01 * max(rq.size, 1)
 
 
