@@ -15,17 +15,22 @@ each case's sizes and data from its own seed:
   up to several leader batches, expert counts up to 1024, skewed and uniform
   expert choice; bit-exact;
 * moe_finalize: row widths on both sides of the wave-per-token layout (K a
-  multiple of 512 or not), a few dropped assignments; bit-exact.
+  multiple of 512 or not), a few dropped assignments; bit-exact;
+* the whole layer (moe_mxfp8_forward) on drawn sizes, routings (plain, Zipf
+  bias, hot and never-chosen experts) and outlier channels: every row of every
+  stage against the oracle, with the weights quantised on the GPU equal to
+  the oracle's.
 """
 import numpy as np
 import pytest
 import torch
 
 import mxfp8_block_scaled_topk_amd as mx
-from gpu_util import (bf16_dev, bf16_host, bf16_rows_rel_err, explain_hq_mismatches, f32_dev, host, i32_dev, i64_dev,
-                      row_rel_err, say, u8_dev)
+import oracle_pool
+from gpu_util import (bf16_dev, bf16_host, bf16_rows_rel_err, check_layer_every_row, explain_hq_mismatches, f32_dev,
+                      host, i32_dev, i64_dev, row_rel_err, say, u8_dev)
 from oracle import moe_ref, mx_ref
-from workloads import to_bf16_bits
+from workloads import custom_config, make_inputs, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -211,3 +216,35 @@ def test_finalize_sweep(seed):
     w_eff = np.where(drop.reshape(T, k), np.float32(0.0), w)
     ref = moe_ref.finalize_ref(y, w_eff, np.where(drop, 0, eri))
     assert np.array_equal(bf16_host(out), ref)
+
+
+@pytest.mark.parametrize("seed", list(range(6)))
+def test_forward_sweep(seed):
+    rng = np.random.default_rng(4000 + seed)
+    # the Zipf bias needs more than its 16 top experts; hot/cold routing
+    # leaves two experts unchosen
+    routing = ["plain", "zipf", "hot_cold"][seed % 3]
+    E = int(rng.choice({"plain": [4, 16, 64, 128], "zipf": [64, 128], "hot_cold": [16, 64]}[routing]))
+    k = min(int(rng.choice([1, 2, 4, 8])), E)
+    T = int(rng.choice([1, 5, 33, 200, 700]))
+    K = int(rng.choice([256, 512, 768]))
+    I = int(rng.choice([128, 256, 384]))
+    outliers = bool(rng.integers(0, 2))
+    cfg = custom_config(f"sweep{seed}", T, K, I, E, k, routing=routing, outliers=outliers)
+    d = make_inputs(cfg, seed=seed)
+    say(f"moe_mxfp8_forward sweep seed={seed} T={T} K={K} I={I} E={E} k={k} routing={routing} outliers={outliers}")
+    w13q, w13s = mx.mx_quantize(bf16_dev(d["w13"]))
+    w2q, w2s = mx.mx_quantize(bf16_dev(d["w2"]))
+    # the oracle quantiser over the worker pool (the same bytes as the serial
+    # routine, pinned in test_oracle_pool.py)
+    r13q, r13s = (a.reshape(E, 2 * I, *a.shape[1:]) for a in oracle_pool.quantize_bf16(d["w13"].reshape(-1, K)))
+    r2q, r2s = (a.reshape(E, K, *a.shape[1:]) for a in oracle_pool.quantize_bf16(d["w2"].reshape(-1, I)))
+    assert np.array_equal(host(w13q), r13q) and np.array_equal(host(w13s), r13s)
+    assert np.array_equal(host(w2q), r2q) and np.array_equal(host(w2s), r2s)
+    ws = mx.forward_workspace(T, K, I, E, k)
+    out = mx.moe_mxfp8_forward(bf16_dev(d["x"]), i32_dev(d["topk_ids"]), f32_dev(d["topk_w"]), w13q, w13s, w2q, w2s,
+                               workspace=ws)
+    torch.cuda.synchronize()
+    inter = {n: host(v) for n, v in mx.forward_intermediates(ws, T, K, I, E, k).items() if n != "y"}
+    inter["y"] = bf16_host(mx.forward_intermediates(ws, T, K, I, E, k)["y"])
+    check_layer_every_row(d, bf16_host(out), inter, r13q, r13s, r2q, r2s, "e4m3", TOL, 5e-2)
