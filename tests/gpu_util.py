@@ -8,6 +8,8 @@ import numpy as np
 import torch
 
 from oracle import mx_ref
+from oracle.moe_ref import router_ref
+from oracle.mx_ref import bf16_to_f64
 
 
 def say(msg):
@@ -215,3 +217,56 @@ def check_layer_every_row(d, out, inter, w13q, w13s, w2q, w2s, w_format, tol, e2
     assert yerr.max() <= tol
     assert e2e.max() <= e2e_tol
     return dict(y_err=float(yerr.max()), e2e=float(e2e.max()), hq_mismatch=n_mis, rows_requant_diff=int(diff.size))
+
+
+# --------------------------------------------------------------------------
+# the GPU router against the router oracle
+# --------------------------------------------------------------------------
+
+U32 = 2.0 ** -24   # float32 unit roundoff
+
+
+def check_router(ids, w, x_bits, gate_bits, bias, k, renormalize):
+    T, K = x_bits.shape
+    E = gate_bits.shape[0]
+    ids_o, _, L = router_ref(x_bits, gate_bits, bias, k, renormalize)
+    xd, gd = bf16_to_f64(x_bits), bf16_to_f64(gate_bits)
+    # |float32 sum - exact| <= K u sum|x g| (any summation order), plus the bias add
+    mag = np.abs(xd) @ np.abs(gd).T
+    fin = np.where(np.isfinite(L), np.abs(L), 0.0)
+    delta = (K * U32 * mag + U32 * fin).max(axis=1) + 1e-30          # per token
+    assert ids.shape == (T, k) and w.shape == (T, k)
+    assert ((ids >= 0) & (ids < E)).all()
+    assert all(len(set(r)) == k for r in ids.tolist()), "repeated expert in a token's selection"
+    srt = -np.sort(-L, axis=1)
+    got = np.take_along_axis(L, ids.astype(np.int64), axis=1)
+    both_inf = np.isneginf(got) & np.isneginf(srt[:, :k])
+    diff = np.where(both_inf, 0.0, np.abs(got - srt[:, :k]))
+    bad = np.argwhere(diff > 2 * delta[:, None])
+    assert bad.size == 0, f"token {bad[0][0]} position {bad[0][1]}: logit off by {diff[tuple(bad[0])]}"
+    if k < E:
+        clear = (srt[:, k - 1] - srt[:, k]) > 2 * delta
+    else:
+        clear = np.ones(T, bool)
+    same = np.sort(ids, axis=1) == np.sort(ids_o, axis=1)
+    assert same[clear].all(), "selection differs where no near-tie decides it"
+    # weights: softmax of the oracle logits over all experts / the GPU's selection
+    z = L - L.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=1, keepdims=True)
+    pw = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    if renormalize:
+        pw = pw / pw.sum(axis=1, keepdims=True)
+    rtol = 4 * delta[:, None] + 1e-5
+    err = np.abs(w - pw) / np.maximum(pw, 1e-30)
+    assert (err <= rtol).all(), f"weight rel err {err.max():.3g}"
+    return int((~clear).sum()), float(err.max())
+
+
+def run_router(x_bits, gate_bits, bias, k, renormalize=True):
+    import mxfp8_block_scaled_topk_amd as mx
+    xb, gb = bf16_dev(x_bits), bf16_dev(gate_bits)
+    bd = None if bias is None else f32_dev(np.asarray(bias, np.float32))
+    ids, w = mx.moe_router(xb, gb, k, bias=bd, renormalize=renormalize)
+    torch.cuda.synchronize()
+    return host(ids), host(w)

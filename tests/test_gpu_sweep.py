@@ -16,6 +16,10 @@ each case's sizes and data from its own seed:
   expert choice; bit-exact;
 * moe_finalize: row widths on both sides of the wave-per-token layout (K a
   multiple of 512 or not), a few dropped assignments; bit-exact;
+* moe_router: token counts around the 64-token workgroup, 2 to 256 experts,
+  no bias, a finite bias or experts barred by a -inf bias, with and without
+  renormalisation; checked as the router tests check it (the selection
+  exact wherever no float32 near-tie decides it);
 * the whole layer (moe_mxfp8_forward) on drawn sizes, routings (plain, Zipf
   bias, hot and never-chosen experts) and outlier channels: every row of every
   stage against the oracle, with the weights quantised on the GPU equal to
@@ -27,8 +31,8 @@ import torch
 
 import mxfp8_block_scaled_topk_amd as mx
 import oracle_pool
-from gpu_util import (bf16_dev, bf16_host, bf16_rows_rel_err, check_layer_every_row, explain_hq_mismatches, f32_dev,
-                      host, i32_dev, i64_dev, row_rel_err, say, u8_dev)
+from gpu_util import (bf16_dev, bf16_host, bf16_rows_rel_err, check_layer_every_row, check_router, explain_hq_mismatches,
+                      f32_dev, host, i32_dev, i64_dev, row_rel_err, run_router, say, u8_dev)
 from oracle import moe_ref, mx_ref
 from workloads import custom_config, make_inputs, to_bf16_bits
 
@@ -248,3 +252,26 @@ def test_forward_sweep(seed):
     inter = {n: host(v) for n, v in mx.forward_intermediates(ws, T, K, I, E, k).items() if n != "y"}
     inter["y"] = bf16_host(mx.forward_intermediates(ws, T, K, I, E, k)["y"])
     check_layer_every_row(d, bf16_host(out), inter, r13q, r13s, r2q, r2s, "e4m3", TOL, 5e-2)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_router_sweep(seed):
+    rng = np.random.default_rng(5000 + seed)
+    E = int(rng.choice([2, 8, 33, 64, 65, 128, 200, 256]))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.choice([1, 63, 64, 65, 1000, 3000]))
+    K = int(rng.choice([64, 192, 1024, 2048]))
+    renorm = bool(rng.integers(0, 2))
+    kind = seed % 3
+    bias = None
+    if kind >= 1:
+        bias = rng.standard_normal(E) * 0.5
+        if kind == 2:                       # some experts never chosen, at least k left
+            bias[rng.choice(E, size=(E - k) // 2, replace=False)] = -np.inf
+    say(f"moe_router sweep seed={seed} T={T} K={K} E={E} k={k} renormalize={renorm} "
+        f"bias={['none', 'finite', 'with -inf'][kind]}")
+    x = rand_bf16(rng, (T, K), 2)
+    gate = to_bf16_bits((rng.standard_normal((E, K)) * 0.02).astype(np.float32))
+    ids, w = run_router(x, gate, bias, k, renorm)
+    near, werr = check_router(ids, w, x, gate, bias, k, renorm)
+    say(f"  tokens with a near-tie at the k-th place {near}, weight rel err {werr:.3g}")
