@@ -23,7 +23,9 @@ each case's sizes and data from its own seed:
 * the whole layer (moe_mxfp8_forward) on drawn sizes, routings (plain, Zipf
   bias, hot and never-chosen experts) and outlier channels: every row of every
   stage against the oracle, with the weights quantised on the GPU equal to
-  the oracle's.
+  the oracle's; the same layer on tile-packed weights gives the same bytes,
+  and with MXFP4 weights (moe_w4a8_forward) meets the same bars;
+* mx_linear (the dense linear) on drawn sizes, every row.
 """
 import numpy as np
 import pytest
@@ -252,6 +254,47 @@ def test_forward_sweep(seed):
     inter = {n: host(v) for n, v in mx.forward_intermediates(ws, T, K, I, E, k).items() if n != "y"}
     inter["y"] = bf16_host(mx.forward_intermediates(ws, T, K, I, E, k)["y"])
     check_layer_every_row(d, bf16_host(out), inter, r13q, r13s, r2q, r2s, "e4m3", TOL, 5e-2)
+    # the same layer on tile-packed weights: the same bytes
+    wp13, wp2 = mx.mx_pack_weights(w13q, mx.PACK_GEMM1), mx.mx_pack_weights(w2q, mx.PACK_GEMM2)
+    out_p = mx.moe_mxfp8_forward_packed(bf16_dev(d["x"]), i32_dev(d["topk_ids"]), f32_dev(d["topk_w"]), wp13, w13s,
+                                        wp2, w2s)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out)
+    # the same layer with the weights quantised to MXFP4 (e2m1) instead
+    del wp13, wp2, out_p
+    f13q, f13s = mx.mx_quantize_fp4(bf16_dev(d["w13"]))
+    f2q, f2s = mx.mx_quantize_fp4(bf16_dev(d["w2"]))
+    g13q, g13s = oracle_pool.quantize_bf16(d["w13"].reshape(-1, K), fp4=True)
+    g2q, g2s = oracle_pool.quantize_bf16(d["w2"].reshape(-1, I), fp4=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(f13q).reshape(g13q.shape), g13q) and np.array_equal(host(f13s).reshape(g13s.shape), g13s)
+    assert np.array_equal(host(f2q).reshape(g2q.shape), g2q) and np.array_equal(host(f2s).reshape(g2s.shape), g2s)
+    out4 = mx.moe_w4a8_forward(bf16_dev(d["x"]), i32_dev(d["topk_ids"]), f32_dev(d["topk_w"]), f13q, f13s, f2q, f2s,
+                               workspace=ws)
+    torch.cuda.synchronize()
+    inter4 = {n: host(v) for n, v in mx.forward_intermediates(ws, T, K, I, E, k).items() if n != "y"}
+    inter4["y"] = bf16_host(mx.forward_intermediates(ws, T, K, I, E, k)["y"])
+    check_layer_every_row(d, bf16_host(out4), inter4, g13q.reshape(E, 2 * I, K // 2), g13s.reshape(E, 2 * I, -1, 2),
+                          g2q.reshape(E, K, I // 2), g2s.reshape(E, K, -1, 2), "e2m1", TOL, 5e-2)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_linear_sweep(seed):
+    rng = np.random.default_rng(6000 + seed)
+    T = int(rng.choice([1, 17, 255, 256, 257, 1000]))
+    K = int(rng.choice([128, 256, 384, 512, 1024]))
+    N = int(rng.choice([256, 512, 768, 1024]))
+    say(f"mx_linear sweep seed={seed} T={T} K={K} N={N}")
+    x = rand_bf16(rng, (T, K), 4)
+    w = to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    wq, ws = mx_ref.mx_quantize_ref(mx_ref.bf16_to_f64(w))
+    y = mx.mx_linear(bf16_dev(x), u8_dev(wq), u8_dev(ws))
+    torch.cuda.synchronize()
+    xq, xs = mx_ref.mx_quantize_ref(mx_ref.bf16_to_f64(x))
+    ref = moe_ref.gmm_mx_ref(xq, xs, wq[None], ws[None], np.array([T], np.int64), 1)
+    err = bf16_rows_rel_err(bf16_host(y), ref)
+    say(f"  max row rel err {err.max():.3g}")
+    assert err.max() <= TOL
 
 
 @pytest.mark.parametrize("seed", SEEDS)
