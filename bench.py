@@ -60,20 +60,31 @@ AHEAD = 8
 # HBM bytes per GEMM1 launch from two rocprofv3 --pmc passes (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for
 # a 1 GiB device-to-device copy in the same run (--copy-calibration).  Valid
-# only for the kernel they were taken on: the SHA-256 of csrc/gmm.hip is
-# checked at run time and the traffic is reported as null on a mismatch.
-GEMM1_TRAFFIC = {"gmm_sha256": "1db8c36d8ad925e8a1b2e6fa3aa34d99f4009bc60a21a300b0fab0a0566b1e40",
+# only for the kernel they were taken on: the digest of csrc/gmm.hip's code
+# (comments and whitespace removed) is checked at run time and the traffic is
+# reported as null on a mismatch.
+GEMM1_TRAFFIC = {"gmm_code_sha256": "d51c062383dcd48b972bd727b89e7fd5744b263bf76cdc48a282b6dd5c20c7d7",
                  "fetch_bytes": 1.2719e+09, "write_bytes": 1.054e+08}
+
+
+def code_digest(path):
+    """SHA-256 of a source file's code: comments and whitespace removed, so
+    that a change to the comments alone keeps the digest."""
+    import hashlib
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return hashlib.sha256(re.sub(r"\s+", "", text).encode()).hexdigest()
 
 
 def gemm1_traffic():
     if not GEMM1_TRAFFIC:
         return None
-    import hashlib
     src = os.path.join(ROOT, "mxfp8_block_scaled_topk_amd", "csrc", "gmm.hip")
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != GEMM1_TRAFFIC["gmm_sha256"]:
-            return None
+    if code_digest(src) != GEMM1_TRAFFIC["gmm_code_sha256"]:
+        return None
     return round(GEMM1_TRAFFIC["fetch_bytes"] + GEMM1_TRAFFIC["write_bytes"])
 
 

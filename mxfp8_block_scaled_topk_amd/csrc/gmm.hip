@@ -48,8 +48,11 @@
 // MFMA pipe idled while both waited).  One barrier per stage sits between
 // the two sub-steps; after it the slot of the current stage is free and the
 // DMA for the stage after next goes into it, a full stage ahead of its use.
-// At the current sizes the kernel is bound by that DMA: with all operands
-// forced L2-resident the same kernel runs about 25 % faster.
+// At the current sizes moving the operands is what bounds the kernel, mostly
+// through the clock it costs under the power limit (measured at the 16K
+// prefill size: without the operand DMA the shader clock rises from about
+// 1.86 to 2.2 GHz and the GEMMs run 15-25 % faster; with every operand an L2
+// hit, 6 % (GEMM1) and 16 % (GEMM2) faster).
 //
 // Scheduling.  The kernel is persistent (one workgroup per CU).  Every
 // workgroup derives the per-expert row ranges and m-tile prefix from the
